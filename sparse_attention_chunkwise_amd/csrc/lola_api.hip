@@ -1,0 +1,263 @@
+// C ABI of liblola: argument checks, layouts and kernel launches.
+// Every check happens on the host before anything is enqueued.
+#include <string.h>
+
+#include "lola_decode.h"
+#include "lola_internal.h"
+#include "lola_misc.h"
+#include "lola_prefill.h"
+
+using namespace lola;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+lola_status make_dims(const lola_config* cfg, Dims* d)
+{
+    if (!cfg) return LOLA_ERR_INVALID_ARG;
+    if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1 || cfg->head_dim < 1 || cfg->feat_half < 1 || cfg->window < 0 ||
+        cfg->cache_cap < 0 || cfg->chunk < 1)
+        return LOLA_ERR_INVALID_ARG;
+    if (cfg->n_q_heads % cfg->n_kv_heads != 0) return LOLA_ERR_INVALID_ARG;
+    if (cfg->n_q_heads / cfg->n_kv_heads > kMaxGroup) return LOLA_ERR_UNSUPPORTED;
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return LOLA_ERR_UNSUPPORTED;
+    if (cfg->feat_half != 32 && cfg->feat_half != 64) return LOLA_ERR_UNSUPPORTED;
+    if (cfg->window > kMaxWindow || cfg->cache_cap > kMaxCache || cfg->chunk > kMaxChunk) return LOLA_ERR_UNSUPPORTED;
+    if (cfg->io_dtype != LOLA_F32 && cfg->io_dtype != LOLA_BF16) return LOLA_ERR_UNSUPPORTED;
+    if (!(cfg->softmax_scale == cfg->softmax_scale)) return LOLA_ERR_INVALID_ARG;  // NaN
+    d->Hq = cfg->n_q_heads;
+    d->Hkv = cfg->n_kv_heads;
+    d->D = cfg->head_dim;
+    d->Fh = cfg->feat_half;
+    d->F = 2 * cfg->feat_half;
+    d->w = cfg->window;
+    d->C = cfg->cache_cap;
+    d->L = cfg->chunk;
+    d->G = cfg->n_q_heads / cfg->n_kv_heads;
+    d->io = cfg->io_dtype;
+    d->esize = cfg->io_dtype == LOLA_BF16 ? 2 : 4;
+    d->tau = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
+    return LOLA_OK;
+}
+
+uint64_t cfg_hash(const lola_config* c, int batch)
+{
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&](uint32_t x) {
+        for (int i = 0; i < 4; ++i) {
+            h ^= (x >> (8 * i)) & 0xffu;
+            h *= 1099511628211ull;
+        }
+    };
+    uint32_t sc;
+    memcpy(&sc, &c->softmax_scale, 4);
+    mix((uint32_t)c->n_q_heads); mix((uint32_t)c->n_kv_heads); mix((uint32_t)c->head_dim);
+    mix((uint32_t)c->feat_half); mix((uint32_t)c->window); mix((uint32_t)c->cache_cap);
+    mix((uint32_t)c->chunk); mix((uint32_t)c->io_dtype); mix(sc); mix((uint32_t)batch);
+    return h;
+}
+
+lola_status check_batch(int32_t batch, const Dims& d)
+{
+    if (batch < 1) return LOLA_ERR_INVALID_ARG;
+    if ((int64_t)batch * d.Hkv > 65535) return LOLA_ERR_UNSUPPORTED;
+    return LOLA_OK;
+}
+
+lola_status hip_status(hipError_t e) { return e == hipSuccess ? LOLA_OK : LOLA_ERR_HIP; }
+
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes)
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+template <int D, int F, typename T>
+lola_status launch_prefill(Args& a, hipStream_t s)
+{
+    const Dims& d = a.d;
+    const int chains = a.B * d.Hkv;
+    dim3 gp((a.wl.X + d.C + 63) / 64, chains);
+    hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return LOLA_ERR_HIP;
+    const size_t scan_lds = scan_smem(D, F, d.C, d.L).total;
+    if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
+    hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(256), scan_lds, s, a);
+    if (hipGetLastError() != hipSuccess) return LOLA_ERR_HIP;
+    const int wpi = (d.G * d.L + 63) / 64;
+    dim3 go(a.NI * wpi, chains);
+    hipLaunchKernelGGL((output_kernel<D, F, T>), go, dim3(256), 0, s, a);
+    return hip_status(hipGetLastError());
+}
+
+template <int D, int F, typename T>
+lola_status launch_decode(Args& a, hipStream_t s)
+{
+    const size_t lds = decode_smem(D, F, a.d.G, a.d.C).total;
+    if (allow_lds(decode_kernel<D, F, T>, lds) != hipSuccess) return LOLA_ERR_HIP;
+    hipLaunchKernelGGL((decode_kernel<D, F, T>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+    return hip_status(hipGetLastError());
+}
+
+#define LOLA_DISPATCH(FN, a, s)                                                          \
+    do {                                                                                 \
+        const Dims& dd = (a).d;                                                          \
+        if (dd.io == LOLA_F32) {                                                         \
+            if (dd.D == 64 && dd.F == 64) return FN<64, 64, float>((a), (s));            \
+            if (dd.D == 64 && dd.F == 128) return FN<64, 128, float>((a), (s));          \
+            if (dd.D == 128 && dd.F == 64) return FN<128, 64, float>((a), (s));          \
+            if (dd.D == 128 && dd.F == 128) return FN<128, 128, float>((a), (s));        \
+        } else {                                                                         \
+            if (dd.D == 64 && dd.F == 64) return FN<64, 64, bf16>((a), (s));             \
+            if (dd.D == 64 && dd.F == 128) return FN<64, 128, bf16>((a), (s));           \
+            if (dd.D == 128 && dd.F == 64) return FN<128, 64, bf16>((a), (s));           \
+            if (dd.D == 128 && dd.F == 128) return FN<128, 128, bf16>((a), (s));         \
+        }                                                                                \
+        return LOLA_ERR_UNSUPPORTED;                                                     \
+    } while (0)
+
+lola_status dispatch_prefill(Args& a, hipStream_t s) { LOLA_DISPATCH(launch_prefill, a, s); }
+lola_status dispatch_decode(Args& a, hipStream_t s) { LOLA_DISPATCH(launch_decode, a, s); }
+
+Args base_args(const Dims& d, int B, void* state)
+{
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.d = d;
+    a.B = B;
+    a.state = (unsigned char*)state;
+    a.sl = state_layout(d, B);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lola_state_bytes(const lola_config* cfg, int32_t batch)
+{
+    Dims d;
+    if (make_dims(cfg, &d) != LOLA_OK || check_batch(batch, d) != LOLA_OK) return 0;
+    return state_layout(d, batch).total;
+}
+
+size_t lola_prefill_workspace_bytes(const lola_config* cfg, int32_t batch, int32_t max_tokens)
+{
+    Dims d;
+    if (make_dims(cfg, &d) != LOLA_OK || check_batch(batch, d) != LOLA_OK || max_tokens < 1) return 0;
+    return ws_layout(d, batch, max_tokens).total;
+}
+
+lola_status lola_init_state(const lola_config* cfg, int32_t batch, const float* W, void* state, void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (!W || !state || !aligned16(W) || !aligned16(state)) return LOLA_ERR_INVALID_ARG;
+    Args a = base_args(d, batch, state);
+    hipLaunchKernelGGL(init_kernel, dim3(batch * d.Hkv + 1), dim3(256), 0, (hipStream_t)stream, a, W,
+                       cfg_hash(cfg, batch));
+    return hip_status(hipGetLastError());
+}
+
+lola_status lola_prefill_chunk(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens, const void* q,
+                               const void* k, const void* v, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (n_tokens < 1) return LOLA_ERR_INVALID_ARG;
+    if (!state || !q || !k || !v || !out || !workspace) return LOLA_ERR_INVALID_ARG;
+    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(workspace))
+        return LOLA_ERR_INVALID_ARG;
+    Args a = base_args(d, batch, state);
+    a.n = n_tokens;
+    a.wl = ws_layout(d, batch, n_tokens);
+    a.NI = a.wl.NI;
+    if (workspace_bytes < a.wl.total) return LOLA_ERR_WORKSPACE;
+    if ((int64_t)a.NI * ((d.G * d.L + 63) / 64) > 0x7fffffff) return LOLA_ERR_UNSUPPORTED;
+    a.ws = (unsigned char*)workspace;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    return dispatch_prefill(a, (hipStream_t)stream);
+}
+
+lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch, const void* q, const void* k,
+                             const void* v, void* out, void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (!state || !q || !k || !v || !out) return LOLA_ERR_INVALID_ARG;
+    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LOLA_ERR_INVALID_ARG;
+    Args a = base_args(d, batch, state);
+    a.n = 1;
+    a.NI = 1;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    return dispatch_decode(a, (hipStream_t)stream);
+}
+
+lola_status lola_read_cache(const lola_config* cfg, const void* state, int32_t batch, int32_t* count, int64_t* pos,
+                            void* k_out, void* v_out, float* H_out, float* s_out, int64_t* tokens_seen, void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (!state || !aligned16(state)) return LOLA_ERR_INVALID_ARG;
+    const void* outs[] = {count, pos, k_out, v_out, H_out, s_out, tokens_seen};
+    for (const void* p : outs)
+        if (p && ((uintptr_t)p & 7u)) return LOLA_ERR_INVALID_ARG;
+    Args a = base_args(d, batch, const_cast<void*>(state));
+    hipStream_t s = (hipStream_t)stream;
+    if (d.io == LOLA_F32)
+        hipLaunchKernelGGL(read_cache_kernel<float>, dim3(batch * d.Hkv), dim3(256), 0, s, a, count, pos,
+                           (float*)k_out, (float*)v_out, H_out, s_out, tokens_seen);
+    else
+        hipLaunchKernelGGL(read_cache_kernel<bf16>, dim3(batch * d.Hkv), dim3(256), 0, s, a, count, pos,
+                           (bf16*)k_out, (bf16*)v_out, H_out, s_out, tokens_seen);
+    return hip_status(hipGetLastError());
+}
+
+lola_status lola_check_state(const lola_config* cfg, const void* state, int32_t batch, void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (!state) return LOLA_ERR_INVALID_ARG;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_ERR_HIP;
+    StateHeader h;
+    if (hipMemcpy(&h, state, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return LOLA_ERR_HIP;
+    if (h.magic != kMagic || h.version != kVersion || h.cfg_hash != cfg_hash(cfg, batch) || h.batch != batch)
+        return LOLA_ERR_BAD_STATE;
+    return LOLA_OK;
+}
+
+const char* lola_status_string(lola_status status)
+{
+    switch (status) {
+    case LOLA_OK: return "ok";
+    case LOLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad count or size)";
+    case LOLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LOLA_ERR_BAD_STATE: return "state header does not match the configuration";
+    case LOLA_ERR_WORKSPACE: return "workspace too small";
+    case LOLA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+// Internal definitions shared by the HIP sources of liblola: the state and
+// workspace layouts, bf16 storage conversion and the MFMA operand traits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lola.h"
+
+namespace lola {
+
+// ---------------------------------------------------------------------------
+// sizes and limits
+// ---------------------------------------------------------------------------
+constexpr int kMaxGroup = 16;     // query heads per KV head
+constexpr int kMaxWindow = 8192;
+constexpr int kMaxCache = 1024;
+constexpr int kMaxChunk = 256;
+constexpr int kMaxCand = kMaxCache + kMaxChunk;  // |cache| + |leaving keys| per interval
+constexpr uint32_t kMagic = 0x414c4f4cu;         // "LOLA"
+constexpr uint32_t kVersion = 1;
+
+inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Dims {
+    int Hq, Hkv, D, Fh, F, w, C, L, G;
+    int io;       // 0 = f32, 1 = bf16
+    int esize;    // bytes per io element
+    float tau;    // softmax scale on q.k
+};
+
+struct StateHeader {
+    uint32_t magic;
+    uint32_t version;
+    uint64_t cfg_hash;
+    int32_t batch;
+    int32_t pad[3];
+};
+
+// State buffer: header | W [Hkv][Fh][D] f32 | chains [B][Hkv]
+// chain: tokens seen i64 | cache_count i32 | H [F][D] f32 | s [F] f32 | cache_pos [C] i32 |
+//        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io
+// Every chain keeps its own token count so that concurrent chains of one
+// sequence never race on a shared counter.  The window ring slot of
+// position p is p % w.
+struct StateLayout {
+    size_t W, chains, chain_bytes;
+    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v;
+    size_t total;
+};
+
+inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
+{
+    StateLayout s;
+    size_t off = 256;
+    s.W = off;
+    off = align_up(off + sizeof(float) * (size_t)d.Hkv * d.Fh * d.D, 256);
+    s.chains = off;
+    size_t c = 0;
+    s.otok = 0;
+    s.ocnt = 8;      c = 256;
+    s.oH = c;        c = align_up(c + sizeof(float) * (size_t)d.F * d.D, 256);
+    s.os = c;        c = align_up(c + sizeof(float) * (size_t)d.F, 256);
+    s.ocpos = c;     c = align_up(c + sizeof(int32_t) * (size_t)(d.C > 0 ? d.C : 1), 256);
+    s.oring_k = c;   c = align_up(c + (size_t)d.esize * d.w * d.D, 256);
+    s.oring_v = c;   c = align_up(c + (size_t)d.esize * d.w * d.D, 256);
+    s.ocache_k = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
+    s.ocache_v = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
+    s.chain_bytes = c;
+    s.total = s.chains + c * (size_t)B * d.Hkv;
+    return s;
+}
+
+// Prefill workspace for one call of n tokens (X = w + n rows of the extended
+// sequence: the window at the call start followed by the new tokens).
+//   t0 [B] i64 | phiX [B][Hkv][X][F] f32 | ring0_k/v [B][Hkv][w][D] io |
+//   cache0_k/v [B][Hkv][C][D] io | cphi [B][Hkv][C][F] f32 |
+//   snapH [B][Hkv][NI][F][D] f32 | snapS [B][Hkv][NI][F] f32 |
+//   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32
+struct WsLayout {
+    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, snapH, snapS, snapRef, snapN;
+    size_t total;
+    int X, NI;
+};
+
+inline __host__ __device__ WsLayout ws_layout(const Dims& d, int B, int n)
+{
+    WsLayout s;
+    s.X = d.w + n;
+    s.NI = (n + d.L - 1) / d.L;
+    size_t ch = (size_t)B * d.Hkv;
+    int Cp = d.C > 0 ? d.C : 1;
+    size_t off = 0;
+    s.t0 = off;       off = align_up(off + sizeof(int64_t) * (size_t)B, 256);
+    s.phiX = off;     off = align_up(off + sizeof(float) * ch * s.X * d.F, 256);
+    s.ring0_k = off;  off = align_up(off + (size_t)d.esize * ch * d.w * d.D, 256);
+    s.ring0_v = off;  off = align_up(off + (size_t)d.esize * ch * d.w * d.D, 256);
+    s.cache0_k = off; off = align_up(off + (size_t)d.esize * ch * Cp * d.D, 256);
+    s.cache0_v = off; off = align_up(off + (size_t)d.esize * ch * Cp * d.D, 256);
+    s.cphi = off;     off = align_up(off + sizeof(float) * ch * Cp * d.F, 256);
+    s.snapH = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F * d.D, 256);
+    s.snapS = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F, 256);
+    s.snapRef = off;  off = align_up(off + sizeof(int32_t) * ch * s.NI * Cp, 256);
+    s.snapN = off;    off = align_up(off + sizeof(int32_t) * ch * s.NI, 256);
+    s.total = off;
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 storage (round to nearest even on store)
+// ---------------------------------------------------------------------------
+struct bf16 {
+    uint16_t x;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.x << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    bf16 r;
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+        r.x = (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+    } else {
+        u += 0x7fffu + ((u >> 16) & 1u);
+        r.x = (uint16_t)(u >> 16);
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand traits.  Both shapes produce a 16x16 f32 tile; lane l holds
+// C[4*(l/16) + i][l%16], i = 0..3.  An A (B) operand lane holds KPL values of
+// row (column) l%16 at contraction slots (l/16)*KPL + j.
+// ---------------------------------------------------------------------------
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct Mma;
+
+template <> struct Mma<float> {       // v_mfma_f32_16x16x4_f32: exact fp32 products
+    static constexpr int KPL = 1;
+    using frag = float;
+    __device__ __forceinline__ static frag pack(const float* v) { return v[0]; }
+    __device__ __forceinline__ static frag zero() { return 0.f; }
+    __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<bf16> {        // v_mfma_f32_16x16x32_bf16 (gfx950)
+    static constexpr int KPL = 8;
+    using frag = bf16x8;
+    __device__ __forceinline__ static frag pack(const float* v)
+    {
+        u16x8 u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = from_f32<bf16>(v[j]).x;
+        return __builtin_bit_cast(bf16x8, u);
+    }
+    __device__ __forceinline__ static frag zero() { return __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0}); }
+    __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// wave helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Kernel argument bundle common to the launches.
+struct Args {
+    Dims d;
+    int B, n, NI;
+    unsigned char* state;
+    unsigned char* ws;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    StateLayout sl;
+    WsLayout wl;
+};
+
+}  // namespace lola
