@@ -1,0 +1,285 @@
+"""Throughput of the LoLA layer hot path on one MI355X.
+
+A step is one lola_prefill_chunk over the 4096-token bf16 GQA workload
+(32 query / 8 KV heads, head_dim 128, feature dim 128, window 64, cache 256,
+interval 64, batch 1): feature rows, the SRE / top-C / fold interval scan and
+the softmax + linear output pass.  Inputs are seeded synthetic tensors already
+resident in HBM; every timed step starts from a freshly initialised state.
+
+Also measured: decode (64 sequences with a 4096-token prefilled state, 256
+single-token steps), per-kernel times from HIP events recorded between the
+library's launches, and the CPU oracle on the host cores as a baseline.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from sparse_attention_chunkwise_amd import inputs as I  # noqa: E402
+from sparse_attention_chunkwise_amd import lola  # noqa: E402
+
+METRIC = "LoLA layer tokens/sec (4K chunkwise prefill; decode) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work, from the interval bookkeeping (data independent)
+# ---------------------------------------------------------------------------
+def interval_plan(layer, T):
+    """Per interval of a fresh state: (a, e, |cache| at start, |leaving|, |U|, |folded|)."""
+    w, C, L = layer.window, layer.cache_cap, layer.chunk
+    cnt, out = 0, []
+    for a in range(0, T, L):
+        e = min(a + L, T)
+        nE = max(0, e - w - max(0, a - w))
+        nU = cnt + nE
+        keep = min(C, nU)
+        out.append((a, e, cnt, nE, nU, nU - keep))
+        cnt = keep
+    return out
+
+
+def algorithmic_work(layer, B, T):
+    """MACs and bytes each prefill kernel must do by definition (per launch)."""
+    D, F, Fh, w, G = layer.head_dim, 2 * layer.feat_half, layer.feat_half, layer.window, layer.group
+    chains = B * layer.n_kv_heads
+    esize = 2 if layer.io_dtype == "bf16" else 4
+    scan = out = 0
+    for a, e, cnt, nE, nU, nF in interval_plan(layer, T):
+        scan += nU * F * (D + 1) + nF * F * (D + 1)          # SRE (n and d) + fold (H and s)
+        for t in range(a, e):
+            nwin = min(w, t + 1)
+            npend = max(0, t - w - max(0, a - w) + 1)
+            out += G * (2 * D * (nwin + cnt) + F * (D + 1) + Fh * D + npend * (F + D + 1))
+    prologue = (w + T) * Fh * D
+    io = B * T * (2 * layer.n_q_heads + 2 * layer.n_kv_heads) * D * esize  # Q, K, V read, O written
+    return {
+        "prologue": {"macs": prologue * chains, "bytes": B * T * layer.n_kv_heads * D * esize},
+        "scan": {"macs": scan * chains, "bytes": B * T * 2 * layer.n_kv_heads * D * esize},
+        "output": {"macs": out * chains, "bytes": io},
+        "layer": {"macs": (scan + out + prologue) * chains, "bytes": io},
+    }
+
+
+def decode_bytes(layer, B):
+    """Bytes one decode step must move: per chain the state it reads and writes."""
+    D, F, w, C = layer.head_dim, 2 * layer.feat_half, layer.window, layer.cache_cap
+    esize = 2 if layer.io_dtype == "bf16" else 4
+    per_chain = 2 * (F * D + F) * 4 + 2 * C * D * esize + 2 * w * D * esize
+    per_chain += (2 * layer.group + 2) * D * esize + 2 * D * esize  # q, out, k, v, slot write
+    return per_chain * B * layer.n_kv_heads
+
+
+def recurrence_bound(layer, B, T, scan_us):
+    """Serial intervals per chain and the measured time per interval of the scan."""
+    n = len(interval_plan(layer, T))
+    return {"intervals": n, "chains": B * layer.n_kv_heads, "us_per_interval": scan_us / n}
+
+
+# ---------------------------------------------------------------------------
+def to_dev(x, layer):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    return t.to(torch.bfloat16) if layer.io_dtype == "bf16" else t
+
+
+def bench_prefill(wl, steps, warmup):
+    L = wl.layer
+    W, Q, K, V = I.make_batch(wl)
+    B, T = wl.batch, wl.seq_len
+    Wd = torch.from_numpy(W).to("cuda")
+    q, k, v = to_dev(Q, L), to_dev(K, L), to_dev(V, L)
+    out = torch.empty_like(q)
+    ws = torch.empty(lola.workspace_bytes(L, B, T), dtype=torch.uint8, device="cuda")
+    states = [lola.init_state(L, B, Wd) for _ in range(steps + warmup)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e4 in ev:  # create the event handles
+        for e in e4:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        lola.prefill(L, states[i], q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lola.prefill_timed(L, states[warmup + i], q, k, v, ev[i], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {"prologue": [], "scan": [], "output": []}
+    total = []
+    for e4 in ev:
+        per["prologue"].append(e4[0].elapsed_time(e4[1]))
+        per["scan"].append(e4[1].elapsed_time(e4[2]))
+        per["output"].append(e4[2].elapsed_time(e4[3]))
+        total.append(e4[0].elapsed_time(e4[3]))
+    ms_step = float(np.mean(total))
+    return {
+        "ms_per_step": ms_step,
+        "wall_ms_per_step": 1000.0 * wall / steps,
+        "kernel_us": {k: 1000.0 * float(np.mean(v)) for k, v in per.items()},
+        "tokens": B * T,
+    }
+
+
+def bench_decode(wl, steps_timed, warmup):
+    """64 sequences: 4096-token prefill (untimed) then `steps_timed` decode steps."""
+    L = wl.layer
+    B, T = wl.batch, wl.seq_len
+    Ks, Vs = [], []
+    W = None
+    for b in range(B):
+        Wb, _, K, V, _ = I.make_sequence(wl, b)
+        if b == 0:
+            W = Wb
+        Ks.append(K)
+        Vs.append(V)
+    Wd = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(W, (L.n_kv_heads,) + W.shape))).to("cuda")
+    k = to_dev(np.stack(Ks), L)
+    v = to_dev(np.stack(Vs), L)
+    del Ks, Vs
+    q = torch.zeros((B, T, L.n_q_heads, L.head_dim), dtype=k.dtype, device="cuda")  # outputs unused here
+    state = lola.init_state(L, B, Wd)
+    lola.prefill(L, state, q, k, v)
+    del q, k, v
+    qd, kd, vd = I.make_decode_steps(wl, steps_timed)
+    qd, kd, vd = to_dev(qd, L), to_dev(kd, L), to_dev(vd, L)
+    outd = torch.empty_like(qd[0])
+    warm = state.clone()
+    for s in range(warmup):
+        lola.decode(L, warm, qd[s], kd[s], vd[s], out=outd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps_timed):
+        lola.decode(L, state, qd[s], kd[s], vd[s], out=outd)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    us_step = 1000.0 * ms / steps_timed
+    nbytes = decode_bytes(L, B)
+    return {
+        "workload": wl.name,
+        "value": B * steps_timed / (ms / 1000.0),
+        "unit": "tokens/s",
+        "us_per_step": us_step,
+        "roofline": {"bound": "hbm", "achieved": nbytes / (us_step * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "bytes_per_launch": nbytes},
+    }
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on the host cores over the same 4096-token workload."""
+    import oracle
+
+    W, Q, K, V = I.make_batch(wl)
+    nthreads = min(os.cpu_count() or 1, wl.batch * wl.layer.n_kv_heads)
+    orc = oracle.Oracle(wl.layer, wl.batch, W)
+    t0 = time.perf_counter()
+    orc.run(Q, K, V, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": wl.batch * wl.seq_len / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"one full pass of the {wl.seq_len}-token workload (all {wl.layer.n_q_heads} query heads), "
+                      f"fp64, {nthreads} threads (one per KV-head chain), {dt:.1f} s"}
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: the LoLA hot path here runs on one GPU; --gpus must be 1 "
+              "(per-(sequence, KV head) chains shard with no collectives; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        copy_calibration()
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.manual_seed(0)
+    wl = I.WORKLOADS[3]
+    L = wl.layer
+    pre = bench_prefill(wl, args.steps, args.warmup)
+    work = algorithmic_work(L, wl.batch, wl.seq_len)
+    ku = pre["kernel_us"]
+    kernels = {}
+    for name in ("prologue", "scan", "output"):
+        us = ku[name]
+        kernels[name] = {"us": us, "tflops": 2 * work[name]["macs"] / (us * 1e-6) / 1e12,
+                         "gbs": work[name]["bytes"] / (us * 1e-6) / 1e9}
+    dom = max(ku, key=ku.get)
+    if dom == "scan":
+        roof = {"bound": "mfma", "achieved": kernels["scan"]["tflops"], "peak": PEAK_TFLOPS["fp32"],
+                "unit": "TFLOP/s"}
+    elif dom == "output":
+        roof = {"bound": "mfma", "achieved": kernels["output"]["tflops"], "peak": PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    tok_s = pre["tokens"] / (pre["ms_per_step"] / 1000.0)
+    layer_bytes = work["layer"]["bytes"]
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len, "q_heads": L.n_q_heads,
+                   "kv_heads": L.n_kv_heads, "head_dim": L.head_dim, "feat_dim": 2 * L.feat_half,
+                   "window": L.window, "cache": L.cache_cap, "chunk": L.chunk},
+        "roofline": roof,
+        "layer_roofline": {"hbm_bytes": layer_bytes, "t_hbm_us": layer_bytes / HBM_PEAK_GBS / 1e3,
+                           "frac_hbm": (layer_bytes / HBM_PEAK_GBS / 1e3) / (pre["ms_per_step"] * 1e3),
+                           "macs": work["layer"]["macs"]},
+        "kernels": kernels,
+        "recurrence": recurrence_bound(L, wl.batch, wl.seq_len, ku["scan"]),
+        "wall_ms_per_step": pre["wall_ms_per_step"],
+    }
+    if not args.no_decode:
+        res["decode"] = bench_decode(I.WORKLOADS[4], args.decode_steps, args.warmup)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,16 @@ lola_status lola_prefill_chunk(const lola_config* cfg, void* state, int32_t batc
                                const void* q, const void* k, const void* v, void* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* lola_prefill_chunk that also records three or four caller-created
+ * hipEvent_t (passed as void*) on `stream`: events[0] before the first
+ * launch, events[1] after the feature-row prologue, events[2] after the
+ * interval scan, events[3] after the output pass.  Any entry may be NULL.
+ * Same results as lola_prefill_chunk; meant for per-kernel timing. */
+lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens,
+                                     const void* q, const void* k, const void* v, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events);
+
 /* One token for every sequence: identical in result to
  * lola_prefill_chunk(n_tokens = 1) (a one-token interval), in one fused launch
  * that needs no workspace.

@@ -74,22 +74,30 @@ hipError_t allow_lds(K kernel, size_t bytes)
                                (int)bytes);
 }
 
+hipError_t mark(void* const* events, int i, hipStream_t s)
+{
+    if (!events || !events[i]) return hipSuccess;
+    return hipEventRecord((hipEvent_t)events[i], s);
+}
+
 template <int D, int F, typename T>
-lola_status launch_prefill(Args& a, hipStream_t s)
+lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
 {
     const Dims& d = a.d;
     const int chains = a.B * d.Hkv;
+    if (mark(ev, 0, s) != hipSuccess) return LOLA_ERR_HIP;
     dim3 gp((a.wl.X + d.C + 63) / 64, chains);
     hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return LOLA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
     const size_t scan_lds = scan_smem(D, F, d.C, d.L).total;
     if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
     hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(256), scan_lds, s, a);
-    if (hipGetLastError() != hipSuccess) return LOLA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
     const int wpi = (d.G * d.L + 63) / 64;
     dim3 go(a.NI * wpi, chains);
     hipLaunchKernelGGL((output_kernel<D, F, T>), go, dim3(256), 0, s, a);
-    return hip_status(hipGetLastError());
+    if (hipGetLastError() != hipSuccess || mark(ev, 3, s) != hipSuccess) return LOLA_ERR_HIP;
+    return LOLA_OK;
 }
 
 template <int D, int F, typename T>
@@ -101,24 +109,24 @@ lola_status launch_decode(Args& a, hipStream_t s)
     return hip_status(hipGetLastError());
 }
 
-#define LOLA_DISPATCH(FN, a, s)                                                          \
+#define LOLA_DISPATCH(FN, ...)                                                           \
     do {                                                                                 \
-        const Dims& dd = (a).d;                                                          \
+        const Dims& dd = a.d;                                                            \
         if (dd.io == LOLA_F32) {                                                         \
-            if (dd.D == 64 && dd.F == 64) return FN<64, 64, float>((a), (s));            \
-            if (dd.D == 64 && dd.F == 128) return FN<64, 128, float>((a), (s));          \
-            if (dd.D == 128 && dd.F == 64) return FN<128, 64, float>((a), (s));          \
-            if (dd.D == 128 && dd.F == 128) return FN<128, 128, float>((a), (s));        \
+            if (dd.D == 64 && dd.F == 64) return FN<64, 64, float>(__VA_ARGS__);         \
+            if (dd.D == 64 && dd.F == 128) return FN<64, 128, float>(__VA_ARGS__);       \
+            if (dd.D == 128 && dd.F == 64) return FN<128, 64, float>(__VA_ARGS__);       \
+            if (dd.D == 128 && dd.F == 128) return FN<128, 128, float>(__VA_ARGS__);     \
         } else {                                                                         \
-            if (dd.D == 64 && dd.F == 64) return FN<64, 64, bf16>((a), (s));             \
-            if (dd.D == 64 && dd.F == 128) return FN<64, 128, bf16>((a), (s));           \
-            if (dd.D == 128 && dd.F == 64) return FN<128, 64, bf16>((a), (s));           \
-            if (dd.D == 128 && dd.F == 128) return FN<128, 128, bf16>((a), (s));         \
+            if (dd.D == 64 && dd.F == 64) return FN<64, 64, bf16>(__VA_ARGS__);          \
+            if (dd.D == 64 && dd.F == 128) return FN<64, 128, bf16>(__VA_ARGS__);        \
+            if (dd.D == 128 && dd.F == 64) return FN<128, 64, bf16>(__VA_ARGS__);        \
+            if (dd.D == 128 && dd.F == 128) return FN<128, 128, bf16>(__VA_ARGS__);      \
         }                                                                                \
         return LOLA_ERR_UNSUPPORTED;                                                     \
     } while (0)
 
-lola_status dispatch_prefill(Args& a, hipStream_t s) { LOLA_DISPATCH(launch_prefill, a, s); }
+lola_status dispatch_prefill(Args& a, hipStream_t s, void* const* ev) { LOLA_DISPATCH(launch_prefill, a, s, ev); }
 lola_status dispatch_decode(Args& a, hipStream_t s) { LOLA_DISPATCH(launch_decode, a, s); }
 
 Args base_args(const Dims& d, int B, void* state)
@@ -167,6 +175,14 @@ lola_status lola_prefill_chunk(const lola_config* cfg, void* state, int32_t batc
                                const void* k, const void* v, void* out, void* workspace, size_t workspace_bytes,
                                void* stream)
 {
+    return lola_prefill_chunk_timed(cfg, state, batch, n_tokens, q, k, v, out, workspace, workspace_bytes, stream,
+                                    nullptr);
+}
+
+lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens,
+                                     const void* q, const void* k, const void* v, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* const* events)
+{
     Dims d;
     lola_status st = make_dims(cfg, &d);
     if (st != LOLA_OK) return st;
@@ -187,7 +203,7 @@ lola_status lola_prefill_chunk(const lola_config* cfg, void* state, int32_t batc
     a.k = k;
     a.v = v;
     a.out = out;
-    return dispatch_prefill(a, (hipStream_t)stream);
+    return dispatch_prefill(a, (hipStream_t)stream, events);
 }
 
 lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch, const void* q, const void* k,

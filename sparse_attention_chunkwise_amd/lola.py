@@ -22,7 +22,7 @@ _STATUS = {0: "LOLA_OK", -1: "LOLA_ERR_INVALID_ARG", -2: "LOLA_ERR_UNSUPPORTED",
 
 # Every symbol include/lola.h declares.
 EXPORTS = ("lola_state_bytes", "lola_prefill_workspace_bytes", "lola_init_state", "lola_prefill_chunk",
-           "lola_decode_step", "lola_read_cache", "lola_check_state", "lola_status_string")
+           "lola_prefill_chunk_timed", "lola_decode_step", "lola_read_cache", "lola_check_state", "lola_status_string")
 
 
 class LolaError(RuntimeError):
@@ -57,6 +57,8 @@ def lib():
         L.lola_init_state.restype = ctypes.c_int
         L.lola_prefill_chunk.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.lola_prefill_chunk.restype = ctypes.c_int
+        L.lola_prefill_chunk_timed.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.lola_prefill_chunk_timed.restype = ctypes.c_int
         L.lola_decode_step.argtypes = [cp, vp, i32, vp, vp, vp, vp, vp]
         L.lola_decode_step.restype = ctypes.c_int
         L.lola_read_cache.argtypes = [cp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -128,6 +130,21 @@ def prefill(layer, state, q, k, v, out=None, workspace=None):
     _check(lib().lola_prefill_chunk(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()), "lola_prefill_chunk")
+    return out
+
+
+def prefill_timed(layer, state, q, k, v, events, out=None, workspace=None):
+    """prefill() that records torch.cuda.Event objects (4, any may be None) around its launches."""
+    B, n = k.shape[0], k.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(layer, B, n), dtype=torch.uint8, device=q.device)
+    handles = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+    _check(lib().lola_prefill_chunk_timed(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(q), _ptr(k),
+                                          _ptr(v), _ptr(out), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(), handles),
+           "lola_prefill_chunk_timed")
     return out
 
 
