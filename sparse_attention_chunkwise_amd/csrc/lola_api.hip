@@ -89,9 +89,9 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     dim3 gp((a.wl.X + d.C + 63) / 64, chains);
     hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
-    const size_t scan_lds = scan_smem(D, F, d.C, d.L).total;
+    const size_t scan_lds = scan_smem(D, F, d.C, d.L, sizeof(T)).total;
     if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
-    hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(256), scan_lds, s, a);
+    hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(scan_threads(D)), scan_lds, s, a);
     if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
     const int wpi = (d.G * d.L + 63) / 64;
     dim3 go(a.NI * wpi, chains);

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
     const T* vE = w == 0 ? vnew : ch.ring_v<T>() + (size_t)(t % (w > 0 ? w : 1)) * D;
 
     // ---- load state, W, queries, the leaving pair ----
-    for (int i = tid; i < F * D; i += 256) Hs[(i / D) * HP + (i % D)] = ch.H()[i];
+    for (int i = tid; i < F * D; i += 256) Hs[(i % F) * HP + (i / F)] = ch.H()[i];  // state H is [D][F]
     for (int i = tid; i < F; i += 256) ss[i] = ch.s()[i];
     const float* W = (const float*)(a.state + a.sl.W) + (size_t)g * Fh * D;
     for (int i = tid; i < Fh * D; i += 256) Ws[(i / D) * (D + 1) + (i % D)] = W[i];
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
         }
         const T* vr = candv(victim);
         for (int i = tid; i < F * D; i += 256) {
-            const int f = i / D, j = i % D;
+            const int f = i % F, j = i / F;
             ch.H()[i] = Hs[f * HP + j] + phf[f] * to_f32(vr[j]);
         }
         for (int f = tid; f < F; f += 256) ch.s()[f] = ss[f] + phf[f];

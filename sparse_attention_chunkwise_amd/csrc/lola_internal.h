@@ -39,7 +39,7 @@ struct StateHeader {
 };
 
 // State buffer: header | W [Hkv][Fh][D] f32 | chains [B][Hkv]
-// chain: tokens seen i64 | cache_count i32 | H [F][D] f32 | s [F] f32 | cache_pos [C] i32 |
+// chain: tokens seen i64 | cache_count i32 | H^T [D][F] f32 | s [F] f32 | cache_pos [C] i32 |
 //        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io
 // Every chain keeps its own token count so that concurrent chains of one
 // sequence never race on a shared counter.  The window ring slot of
@@ -76,10 +76,12 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 // sequence: the window at the call start followed by the new tokens).
 //   t0 [B] i64 | phiX [B][Hkv][X][F] f32 | ring0_k/v [B][Hkv][w][D] io |
 //   cache0_k/v [B][Hkv][C][D] io | cphi [B][Hkv][C][F] f32 |
-//   snapH [B][Hkv][NI][F][D] f32 | snapS [B][Hkv][NI][F] f32 |
+//   phiS [B][Hkv][X][2F] bf16 | cphiS [B][Hkv][C][2F] bf16 (hi then lo parts of
+//   phi, features in the SRE operand order) |
+//   snapH [B][Hkv][NI][D][F] f32 (H^T) | snapS [B][Hkv][NI][F] f32 |
 //   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32
 struct WsLayout {
-    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, snapH, snapS, snapRef, snapN;
+    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, snapH, snapS, snapRef, snapN;
     size_t total;
     int X, NI;
 };
@@ -99,6 +101,8 @@ inline __host__ __device__ WsLayout ws_layout(const Dims& d, int B, int n)
     s.cache0_k = off; off = align_up(off + (size_t)d.esize * ch * Cp * d.D, 256);
     s.cache0_v = off; off = align_up(off + (size_t)d.esize * ch * Cp * d.D, 256);
     s.cphi = off;     off = align_up(off + sizeof(float) * ch * Cp * d.F, 256);
+    s.phiS = off;     off = align_up(off + sizeof(uint16_t) * ch * s.X * 2 * d.F, 256);
+    s.cphiS = off;    off = align_up(off + sizeof(uint16_t) * ch * Cp * 2 * d.F, 256);
     s.snapH = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F * d.D, 256);
     s.snapS = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F, 256);
     s.snapRef = off;  off = align_up(off + sizeof(int32_t) * ch * s.NI * Cp, 256);

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void read_cache_kernel(Args a, int32_t* count,
         }
     }
     if (H_out)
-        for (int i = threadIdx.x; i < F * D; i += 256) H_out[(size_t)chain * F * D + i] = ch.H()[i];
+        for (int i = threadIdx.x; i < F * D; i += 256) H_out[(size_t)chain * F * D + i] = ch.H()[(i % D) * F + i / D];
     if (s_out)
         for (int i = threadIdx.x; i < F; i += 256) s_out[(size_t)chain * F + i] = ch.s()[i];
 }

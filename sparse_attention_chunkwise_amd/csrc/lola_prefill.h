@@ -90,6 +90,26 @@ __device__ __forceinline__ float* ws_cphi(const Args& a, int chain, int slot)
     int Cp = a.d.C > 0 ? a.d.C : 1;
     return (float*)(a.ws + a.wl.cphi) + ((size_t)chain * Cp + slot) * a.d.F;
 }
+// bf16 hi/lo split rows of phi (2F values: hi parts, then lo parts), features
+// permuted so that an MFMA operand lane reads 8 contiguous values.
+__device__ __forceinline__ uint16_t* ws_phiS(const Args& a, int chain, int x)
+{
+    return (uint16_t*)(a.ws + a.wl.phiS) + ((size_t)chain * a.wl.X + x) * 2 * a.d.F;
+}
+__device__ __forceinline__ uint16_t* ws_cphiS(const Args& a, int chain, int slot)
+{
+    int Cp = a.d.C > 0 ? a.d.C : 1;
+    return (uint16_t*)(a.ws + a.wl.cphiS) + ((size_t)chain * Cp + slot) * 2 * a.d.F;
+}
+// Operand position of feature f: MFMA step m = f/32, lane group qg = (f%16)/4,
+// slot j = 4*((f/16)%2) + f%4, position m*32 + qg*8 + j.  Lane group qg of an
+// accumulator tile holds rows qg*4..qg*4+3, so tiles ft = 2m and 2m+1 of H feed
+// MFMA step m without any exchange between lanes.
+__device__ __forceinline__ int perm_pos(int f)
+{
+    const int ft = f >> 4, r = f & 15;
+    return (ft >> 1) * 32 + (r >> 2) * 8 + (ft & 1) * 4 + (r & 3);
+}
 
 // ---------------------------------------------------------------------------
 // 1. prologue: phi rows + call-start copies.  grid (ceil((X + C) / 64), B*Hkv)
@@ -118,8 +138,10 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
         T* cpk = nullptr;
         T* cpv = nullptr;
         float* phi_out = nullptr;
+        uint16_t* phs_out = nullptr;
         if (row < X) {
             phi_out = ws_phiX(a, chain, row);
+            phs_out = ws_phiS(a, chain, row);
             if (row < w) {
                 int64_t p = t0 - w + row;
                 cpk = (T*)(a.ws + a.wl.ring0_k) + ((size_t)chain * w + row) * D;
@@ -135,6 +157,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
         } else if (row < X + C) {
             int i = row - X;
             phi_out = ws_cphi(a, chain, i);
+            phs_out = ws_cphiS(a, chain, i);
             int Cp = C > 0 ? C : 1;
             cpk = (T*)(a.ws + a.wl.cache0_k) + ((size_t)chain * Cp + i) * D;
             cpv = (T*)(a.ws + a.wl.cache0_v) + ((size_t)chain * Cp + i) * D;
@@ -167,74 +190,176 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
         float en = lane < Fh ? expf(zmin - z) : 0.f;
         float sp = wave_sum(ep), sn = wave_sum(en);
         if (lane < Fh) {
-            bool valid = src != nullptr;
-            phi_out[lane] = valid ? ep / sp : 0.f;
-            phi_out[Fh + lane] = valid ? en / sn : 0.f;
+            const bool valid = src != nullptr;
+            const float p0 = valid ? ep / sp : 0.f, p1 = valid ? en / sn : 0.f;
+            phi_out[lane] = p0;
+            phi_out[Fh + lane] = p1;
+            const uint16_t h0 = from_f32<bf16>(p0).x, h1 = from_f32<bf16>(p1).x;
+            const int q0 = perm_pos(lane), q1 = perm_pos(Fh + lane);
+            phs_out[q0] = h0;
+            phs_out[q1] = h1;
+            phs_out[2 * Fh + q0] = from_f32<bf16>(p0 - __uint_as_float((uint32_t)h0 << 16)).x;
+            phs_out[2 * Fh + q1] = from_f32<bf16>(p1 - __uint_as_float((uint32_t)h1 << 16)).x;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// 2. scan: one workgroup per chain, intervals in order.
+// 2. scan: one workgroup per chain (D/16 waves), intervals in order.
+//
+//   Wave w owns columns [16w, 16w+16) of H: its F/16 accumulator tiles of
+//   H[f][d] stay in registers across the whole call.  The same registers,
+//   split into bf16 hi/lo parts, are the A operand of the SRE contraction
+//   n^T = H^T phi^T for those columns, computed with three bf16 MFMAs
+//   (hi.hi + lo.hi + hi.lo; each product accurate to about 2^-16 of its
+//   terms, far inside the selection margin).  Every wave sees every
+//   candidate: candidate phi rows (pre-split hi/lo by the prologue) and
+//   values are staged through LDS 64 candidates at a time with the next
+//   batch prefetched into registers; per-wave partial errors are summed in a
+//   fixed order.  d = phi . s uses hi + lo in fp32.  Top-C is an exact
+//   selection on (SRE desc, position asc): a 256-bin histogram over the SRE
+//   bit patterns finds the boundary bin, whose few members are ranked
+//   pairwise.  The fold stages up to 32 folded pairs transposed in LDS and
+//   adds phi(k) v^T with phi split in three bf16 parts (exact; bf16 io, where
+//   v is exact in bf16) or with fp32 MFMA (fp32 io).
 // ---------------------------------------------------------------------------
+constexpr int kSelBins = 256;
+constexpr int kBatch = 64;      // candidates staged per SRE batch
+constexpr int kFoldChunk = 64;  // folded pairs staged per fold chunk
+
+__host__ __device__ constexpr int scan_threads(int D) { return 4 * D; }  // D/16 waves
+
 struct ScanSmem {
-    // byte offsets into dynamic LDS
-    size_t H, s, esc, upos, keep, cref, cpos, fold, freed, keptE, misc, total;
+    size_t stage, part, ebits, keep, fold, memb, freed, keptE, cref, cpos, hist, s, dS, misc, total;
+    int sphi_stride, sv_stride;  // elements per staged phi row (bf16) / value row
 };
 
-__host__ __device__ inline ScanSmem scan_smem(int D, int F, int C, int L)
+__host__ __device__ inline ScanSmem scan_smem(int D, int F, int C, int L, int esize)
 {
     ScanSmem m;
-    int U = C + L;
-    int Cp = C > 0 ? C : 1;
+    const int U = C + L, Cp = C > 0 ? C : 1, NW = D / 16;
+    m.sphi_stride = 2 * F + 8;
+    m.sv_stride = D + (esize == 2 ? 8 : 4);
+    const size_t sre_stage = (size_t)kBatch * (2 * m.sphi_stride + esize * m.sv_stride);
+    const size_t EP = kFoldChunk + 8;
+    const size_t fold_stage = esize == 2 ? 2 * EP * (3 * (size_t)F + D) : 4 * (kFoldChunk + 4) * ((size_t)F + D);
     size_t off = 0;
-    m.H = off;     off += sizeof(float) * (size_t)F * (D + 4);
-    m.s = off;     off += sizeof(float) * F;
-    m.esc = off;   off += sizeof(float) * U;
-    m.upos = off;  off += sizeof(int) * U;
+    m.stage = off; off += align_up(sre_stage > fold_stage ? sre_stage : fold_stage, 16);
+    m.part = off;  off += sizeof(float) * (size_t)NW * U;
+    m.ebits = off; off += sizeof(uint32_t) * U;
     m.keep = off;  off += sizeof(int) * U;
-    m.cref = off;  off += sizeof(int) * Cp;
-    m.cpos = off;  off += sizeof(int) * Cp;
     m.fold = off;  off += sizeof(int) * U;
+    m.memb = off;  off += sizeof(int) * U;
     m.freed = off; off += sizeof(int) * Cp;
     m.keptE = off; off += sizeof(int) * (L + 1);
-    m.misc = off;  off += sizeof(int) * 8;
+    m.cref = off;  off += sizeof(int) * Cp;
+    m.cpos = off;  off += sizeof(int) * Cp;
+    m.hist = off;  off += sizeof(int) * kSelBins;
+    m.s = off;     off += sizeof(float) * F;
+    m.dS = off;    off += sizeof(float) * kBatch;
+    m.misc = off;  off += sizeof(int) * 16;
     m.total = align_up(off, 16);
     return m;
 }
 
-template <int D, int F, typename T>
-__global__ __launch_bounds__(256) void scan_kernel(Args a)
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ void load4(const float* p, float* o)
 {
-    constexpr int NW = 4, HP = D + 4;
+    const float4 t = *(const float4*)p;
+    o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* o)
+{
+    const uint2 t = *(const uint2*)p;
+    o[0] = __uint_as_float(t.x << 16);
+    o[1] = __uint_as_float(t.x & 0xffff0000u);
+    o[2] = __uint_as_float(t.y << 16);
+    o[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+template <int D, int F, typename T>
+__global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
+{
+    constexpr int NT = scan_threads(D), NW = D / 16, FT = F / 16, FM = F / 32;
+    constexpr int NB = kSelBins, BATCH = kBatch, EC = kFoldChunk;
+    constexpr bool BF = sizeof(T) == 2;
+    constexpr int VU = BF ? 8 : 4;                  // values per 16-byte unit
+    constexpr int PU_ROW = (2 * F) / 8;              // 16-byte units per phi split row
+    constexpr int VU_ROW = D / VU;                   // 16-byte units per value row
+    constexpr int PU_PT = (BATCH * PU_ROW + NT - 1) / NT;
+    constexpr int VU_PT = (BATCH * VU_ROW + NT - 1) / NT;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
-    const ScanSmem sm = scan_smem(D, F, C, L);
-    float* Hs = (float*)(smem + sm.H);
-    float* ss = (float*)(smem + sm.s);
-    float* esc = (float*)(smem + sm.esc);
-    int* upos = (int*)(smem + sm.upos);
+    const ScanSmem sm = scan_smem(D, F, C, L, sizeof(T));
+    const int SPS = sm.sphi_stride, SVS = sm.sv_stride;
+    uint16_t* stP = (uint16_t*)(smem + sm.stage);                   // [BATCH][SPS]
+    T* stV = (T*)(smem + sm.stage + sizeof(uint16_t) * BATCH * SPS);  // [BATCH][SVS]
+    float* part = (float*)(smem + sm.part);
+    uint32_t* ebits = (uint32_t*)(smem + sm.ebits);
     int* keep = (int*)(smem + sm.keep);
-    int* cref = (int*)(smem + sm.cref);
-    int* cpos = (int*)(smem + sm.cpos);
     int* fold = (int*)(smem + sm.fold);
+    int* memb = (int*)(smem + sm.memb);
     int* freed = (int*)(smem + sm.freed);
     int* keptE = (int*)(smem + sm.keptE);
+    int* cref = (int*)(smem + sm.cref);
+    int* cpos = (int*)(smem + sm.cpos);
+    int* hist = (int*)(smem + sm.hist);
+    float* sP = (float*)(smem + sm.s);  // s in operand (perm_pos) order
+    float* dS = (float*)(smem + sm.dS);
     int* misc = (int*)(smem + sm.misc);
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ws_t0(a, b);
-    const int n = a.n, NI = a.NI, X = a.wl.X;
+    const int n = a.n, NI = a.NI;
     const int Cp = C > 0 ? C : 1;
+    const int U = C + L;
 
-    // load the state of this chain
-    for (int i = tid; i < F * D; i += 256) Hs[(i / D) * HP + (i % D)] = ch.H()[i];
-    for (int i = tid; i < F; i += 256) ss[i] = ch.s()[i];
+    // ---- state in: this wave's column tiles of H to registers ----
+    floatx4 Hr[FT];  // Hr[ft][i] = H[ft*16 + qg*4 + i][wave*16 + r16]
+    const float* Hst = ch.H();  // [D][F]
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+        const float4 t4 = *(const float4*)(Hst + (size_t)(wave * 16 + r16) * F + ft * 16 + qg * 4);
+        Hr[ft] = floatx4{t4.x, t4.y, t4.z, t4.w};
+    }
+    bf16x8 Ah[FM], Al[FM];  // SRE A operand: row d = wave*16 + r16, slot (qg, j) <-> feature of perm_pos
+    auto split_H = [&]() {
+#pragma unroll
+        for (int m = 0; m < FM; ++m) {
+            u16x8 h, l;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = Hr[2 * m + (j >> 2)][j & 3];
+                const uint16_t hb = bf16_bits(x);
+                h[j] = hb;
+                l[j] = bf16_bits(x - bf16_val(hb));
+            }
+            Ah[m] = __builtin_bit_cast(bf16x8, h);
+            Al[m] = __builtin_bit_cast(bf16x8, l);
+        }
+    };
+    split_H();
+    for (int i = tid; i < F; i += NT) sP[perm_pos(i)] = ch.s()[i];
     int cnt = min(max(ch.cnt(), 0), C);
-    for (int i = tid; i < cnt; i += 256) {
+    for (int i = tid; i < cnt; i += NT) {
         cpos[i] = ch.cpos()[i];
         cref[i] = -(i + 1);
     }
@@ -249,116 +374,223 @@ __global__ __launch_bounds__(256) void scan_kernel(Args a)
         const int64_t ap = t0 + (int64_t)c * L;
         const int64_t ep = ap + L < t0 + n ? ap + L : t0 + n;
 
-        // ---- interval-start snapshot for the output pass ----
+        // ---- interval-start snapshot (H^T [D][F], s, cache refs) ----
         {
-            float* dst = snapH + (size_t)c * F * D;
-            for (int i = tid; i < F * D / 4; i += 256) {
-                int f = (i * 4) / D, col = (i * 4) % D;
-                *(float4*)(dst + (size_t)f * D + col) = *(const float4*)(Hs + f * HP + col);
-            }
-            for (int i = tid; i < F; i += 256) snapS[(size_t)c * F + i] = ss[i];
-            for (int i = tid; i < cnt; i += 256) snapRef[(size_t)c * Cp + i] = cref[i];
+            float* dst = snapH + (size_t)c * F * D + (size_t)(wave * 16 + r16) * F + qg * 4;
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft)
+                *(float4*)(dst + ft * 16) = make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
+            for (int i = tid; i < F; i += NT) snapS[(size_t)c * F + i] = sP[perm_pos(i)];
+            for (int i = tid; i < cnt; i += NT) snapRef[(size_t)c * Cp + i] = cref[i];
             if (tid == 0) snapN[c] = cnt;
         }
 
-        // ---- candidates: cache slots [0, cnt) then leaving keys ----
+        // ---- candidates: cache slots [0, cnt) then the keys leaving the window ----
         const int64_t eS = ap - w > 0 ? ap - w : 0;
-        const int64_t eE = ep - w;  // exclusive
+        const int64_t eE = ep - w;
         const int nE = eE > eS ? (int)(eE - eS) : 0;
         const int nU = cnt + nE;
-        const int xE0 = (int)(eS - (t0 - w));  // X row of the first leaving key
-        for (int u = tid; u < nU; u += 256) upos[u] = u < cnt ? cpos[u] : (int)(eS + (u - cnt));
-
+        const int xE0 = (int)(eS - (t0 - w));
         auto cand_phi = [&](int u) -> const float* {
-            return u < cnt ? ws_cphi(a, chain, u) : ws_phiX(a, chain, xE0 + (u - cnt));
+            if (u >= cnt) return ws_phiX(a, chain, xE0 + (u - cnt));
+            const int r = cref[u];
+            return r >= 0 ? ws_phiX(a, chain, r) : ws_cphi(a, chain, -r - 1);
+        };
+        auto cand_phs = [&](int u) -> const uint16_t* {
+            if (u >= cnt) return ws_phiS(a, chain, xE0 + (u - cnt));
+            const int r = cref[u];
+            return r >= 0 ? ws_phiS(a, chain, r) : ws_cphiS(a, chain, -r - 1);
         };
         auto cand_v = [&](int u) -> const T* {
             return u < cnt ? ref_v<T>(a, chain, b, g, cref[u]) : xrow_v<T>(a, chain, b, g, xE0 + (u - cnt));
         };
+        auto cand_pos = [&](int u) -> int { return u < cnt ? cpos[u] : (int)(eS + (u - cnt)); };
+
+        // ---- SRE in batches of 64 candidates ----
+        const int nbat = (nU + BATCH - 1) / BATCH;
+        uint4 pre_p[PU_PT], pre_v[VU_PT];
+        auto prefetch = [&](int bi) {
+#pragma unroll
+            for (int k = 0; k < PU_PT; ++k) {
+                const int idx = tid + k * NT;
+                const int cl = idx / PU_ROW, un = idx % PU_ROW, u = bi * BATCH + cl;
+                pre_p[k] = (idx < BATCH * PU_ROW && u < nU) ? *(const uint4*)(cand_phs(u) + un * 8)
+                                                            : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < VU_PT; ++k) {
+                const int idx = tid + k * NT;
+                const int cl = idx / VU_ROW, un = idx % VU_ROW, u = bi * BATCH + cl;
+                pre_v[k] = (idx < BATCH * VU_ROW && u < nU) ? *(const uint4*)(cand_v(u) + un * VU)
+                                                            : make_uint4(0, 0, 0, 0);
+            }
+        };
+        if (nbat > 0) prefetch(0);
+        for (int bi = 0; bi < nbat; ++bi) {
+            __syncthreads();  // the previous batch is consumed
+#pragma unroll
+            for (int k = 0; k < PU_PT; ++k) {
+                const int idx = tid + k * NT;
+                if (idx < BATCH * PU_ROW) *(uint4*)(stP + (idx / PU_ROW) * SPS + (idx % PU_ROW) * 8) = pre_p[k];
+            }
+#pragma unroll
+            for (int k = 0; k < VU_PT; ++k) {
+                const int idx = tid + k * NT;
+                if (idx < BATCH * VU_ROW) *(uint4*)(stV + (idx / VU_ROW) * SVS + (idx % VU_ROW) * VU) = pre_v[k];
+            }
+            __syncthreads();
+            if (bi + 1 < nbat) prefetch(bi + 1);
+            {
+                // d = phi . s for the staged candidates, (hi + lo) parts in fp32;
+                // wave w takes BATCH/NW candidates, LPC lanes per candidate
+                constexpr int CPW = BATCH / NW, LPC = 64 / CPW, PPL = F / LPC;
+                const int cl = wave * CPW + lane / LPC, sub = lane % LPC;
+                const uint16_t* pr = stP + cl * SPS + sub * PPL;
+                float dd = 0.f;
+#pragma unroll
+                for (int p = 0; p < PPL; p += 8) {
+                    const uint4 hq = *(const uint4*)(pr + p);
+                    const uint4 lq = *(const uint4*)(pr + F + p);
+                    const float4 s0 = *(const float4*)(sP + sub * PPL + p);
+                    const float4 s1 = *(const float4*)(sP + sub * PPL + p + 4);
+                    const uint32_t hw[4] = {hq.x, hq.y, hq.z, hq.w}, lw[4] = {lq.x, lq.y, lq.z, lq.w};
+                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float hv = __uint_as_float((j & 1) ? (hw[j >> 1] & 0xffff0000u) : (hw[j >> 1] << 16));
+                        const float lv = __uint_as_float((j & 1) ? (lw[j >> 1] & 0xffff0000u) : (lw[j >> 1] << 16));
+                        dd += (hv + lv) * sv[j];
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < LPC; o <<= 1) dd += __shfl_xor(dd, o, 64);
+                if (sub == 0) dS[cl] = dd;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int tl = 0; tl < BATCH / 16; tl += 2) {
+                if (bi * BATCH + tl * 16 >= nU) break;  // wave-uniform; rows past nU are zero-filled
+                floatx4 acc[2], acc2[2];
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) acc[t2] = acc2[t2] = floatx4{0.f, 0.f, 0.f, 0.f};
+                const uint16_t* pr0 = stP + (tl * 16 + r16) * SPS + qg * 8;
+                const uint16_t* pr1 = pr0 + 16 * SPS;
+#pragma unroll
+                for (int m = 0; m < FM; ++m) {
+                    const bf16x8 h0 = *(const bf16x8*)(pr0 + m * 32);
+                    const bf16x8 h1 = *(const bf16x8*)(pr1 + m * 32);
+                    const bf16x8 l0 = *(const bf16x8*)(pr0 + F + m * 32);
+                    const bf16x8 l1 = *(const bf16x8*)(pr1 + F + m * 32);
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah[m], h0, acc[0], 0, 0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah[m], h1, acc[1], 0, 0, 0);
+                    acc2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al[m], h0, acc2[0], 0, 0, 0);
+                    acc2[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al[m], h1, acc2[1], 0, 0, 0);
+                    acc2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah[m], l0, acc2[0], 0, 0, 0);
+                    acc2[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah[m], l1, acc2[1], 0, 0, 0);
+                }
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int cl = (tl + t2) * 16 + r16;
+                    const int u = bi * BATCH + cl;
+                    const float dpart = dS[cl];
+                    const float inv = dpart > 0.f ? 1.0f / dpart : 0.f;
+                    // n[d = wave*16 + qg*4 + i][candidate u] = acc + acc2
+                    float vv[4];
+                    load4(stV + cl * SVS + wave * 16 + qg * 4, vv);
+                    float e = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float df = (acc[t2][i] + acc2[t2][i]) * inv - vv[i];
+                        e += df * df;
+                    }
+                    e += __shfl_xor(e, 16, 64);
+                    e += __shfl_xor(e, 32, 64);
+                    if (qg == 0 && u < nU) part[wave * U + u] = e;
+                }
+            }
+        }
+        __syncthreads();
+        for (int u = tid; u < nU; u += NT) {
+            float e = part[u];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) e += part[ww * U + u];
+            ebits[u] = __float_as_uint(e);
+        }
         __syncthreads();
 
-        // ---- SRE of every candidate against the interval-start state ----
-        // n^T tile: acc[ct] = phi(k_u) . H[:, 16ct + r16] for 16 candidates per
-        // tile (f32 MFMA, exact fp32 products); d_u = phi(k_u) . s.
-        for (int tile = wave; tile * 16 < nU; tile += NW) {
-            const int u = tile * 16 + r16;
-            float av[F / 4];
-            if (u < nU) {
-                const float* ph = cand_phi(u) + qg * (F / 4);
+        // ---- exact top-C on (SRE desc, position asc), then compaction: wave 0 ----
+        if (wave == 0) {
+            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            if (nU > C && C == 0) {
+                for (int u = lane; u < nU; u += 64) keep[u] = 0;
+            } else if (nU > C) {
+                uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll 4
+                for (int u = lane; u < nU; u += 64) { lo = min(lo, ebits[u]); hi = max(hi, ebits[u]); }
+                const uint32_t minb = wave_min_u32(lo);
+                // monotone bin of an SRE bit pattern (same formula in both passes)
+                const float bscale = (float)NB / ((float)(wave_max_u32(hi) - minb) + 1.0f);
+                auto bin_of = [&](uint32_t x) { return min(NB - 1, (int)((float)(x - minb) * bscale)); };
 #pragma unroll
-                for (int m = 0; m < F / 4; m += 4) {
-                    float4 t4 = *(const float4*)(ph + m);
-                    av[m] = t4.x; av[m + 1] = t4.y; av[m + 2] = t4.z; av[m + 3] = t4.w;
+                for (int k = 0; k < NB / 64; ++k) hist[lane * (NB / 64) + k] = 0;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll 4
+                for (int u = lane; u < nU; u += 64) atomicAdd(&hist[bin_of(ebits[u])], 1);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                // lane l holds bins NB-1-4l .. NB-4-4l (highest first)
+                int cb[4], tot = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { cb[k] = hist[NB - 1 - (4 * lane + k)]; tot += cb[k]; }
+                int incl = tot;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int up = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += up;
+                }
+                const int excl = incl - tot;
+                int bsel = -1, above = 0;
+                if (excl < C && incl >= C) {
+                    int cum = excl;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (bsel < 0 && cum + cb[k] >= C) { bsel = NB - 1 - (4 * lane + k); above = cum; }
+                        cum += cb[k];
+                    }
+                }
+                const uint64_t hit = __ballot(bsel >= 0);
+                const int src = __ffsll((long long)hit) - 1;
+                const int bstar = __shfl(bsel, src, 64);
+                const int need = C - __shfl(above, src, 64);
+                int m = 0;
+#pragma unroll 4
+                for (int base = 0; base < nU; base += 64) {
+                    const int u = base + lane;
+                    const int bin = u < nU ? bin_of(ebits[u]) : -1;
+                    if (u < nU && bin != bstar) keep[u] = bin > bstar;
+                    const bool mb = u < nU && bin == bstar;
+                    const uint64_t bm = __ballot(mb);
+                    if (mb) memb[m + __popcll(bm & lt)] = u;
+                    m += __popcll(bm);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                for (int i = lane; i < m; i += 64) {
+                    const int u = memb[i];
+                    const uint32_t eu = ebits[u];
+                    const int pu = cand_pos(u);
+                    int rank = 0;
+                    for (int j2 = 0; j2 < m; ++j2) {
+                        const int v2 = memb[j2];
+                        const uint32_t ev = ebits[v2];
+                        rank += (ev > eu) || (ev == eu && cand_pos(v2) < pu);
+                    }
+                    keep[u] = rank < need;
                 }
             } else {
-#pragma unroll
-                for (int m = 0; m < F / 4; ++m) av[m] = 0.f;
+                for (int u = lane; u < nU; u += 64) keep[u] = 1;
             }
-            floatx4 acc[D / 16];
-#pragma unroll
-            for (int ct = 0; ct < D / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-            float dpart = 0.f;
-#pragma unroll 4
-            for (int m = 0; m < F / 4; ++m) {
-                const int f = qg * (F / 4) + m;
-                dpart += av[m] * ss[f];
-#pragma unroll
-                for (int ct = 0; ct < D / 16; ++ct)
-                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], Hs[f * HP + ct * 16 + r16], acc[ct], 0, 0, 0);
-            }
-            dpart += __shfl_xor(dpart, 16, 64);
-            dpart += __shfl_xor(dpart, 32, 64);
-            float err[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = qg * 4 + i;
-                const int uu = tile * 16 + row;
-                const float drow = __shfl(dpart, row, 64);
-                const T* vr = uu < nU ? cand_v(uu) : nullptr;
-                float e = 0.f;
-#pragma unroll
-                for (int ct = 0; ct < D / 16; ++ct) {
-                    float r = drow > 0.f ? acc[ct][i] / drow : 0.f;
-                    float vv = vr ? to_f32(vr[ct * 16 + r16]) : 0.f;
-                    float df = r - vv;
-                    e += df * df;
-                }
-                err[i] = e;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float e = err[i];
-                e += __shfl_xor(e, 1, 64);
-                e += __shfl_xor(e, 2, 64);
-                e += __shfl_xor(e, 4, 64);
-                e += __shfl_xor(e, 8, 64);
-                const int uu = tile * 16 + qg * 4 + i;
-                if (r16 == 0 && uu < nU) esc[uu] = e;
-            }
-        }
-        __syncthreads();
-
-        // ---- keep the C highest by (SRE desc, position asc) ----
-        for (int u = tid; u < nU; u += 256) {
-            int kp = 1;
-            if (nU > C) {
-                const uint32_t eu = __float_as_uint(esc[u]);
-                const int pu = upos[u];
-                int rank = 0;
-                for (int v2 = 0; v2 < nU; ++v2) {
-                    const uint32_t ev = __float_as_uint(esc[v2]);
-                    rank += (ev > eu) || (ev == eu && upos[v2] < pu);
-                }
-                kp = rank < C;
-            }
-            keep[u] = kp;
-        }
-        __syncthreads();
-
-        // ---- compaction (wave 0): fold list, freed slots, kept leaving keys ----
-        if (wave == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             int nF = 0, nFr = 0, nK = 0;
-            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll 4
             for (int base = 0; base < nU; base += 64) {
                 const int u = base + lane;
                 const bool valid = u < nU;
@@ -374,68 +606,131 @@ __global__ __launch_bounds__(256) void scan_kernel(Args a)
                 nFr += __popcll(bFr);
                 nK += __popcll(bK);
             }
-            if (lane == 0) { misc[0] = nF; misc[1] = nFr; misc[2] = nK; }
+            if (lane == 0) { misc[5] = nF; misc[6] = nFr; misc[7] = nK; }
         }
         __syncthreads();
-        const int nF = misc[0], nFr = misc[1], nK = misc[2];
+        const int nF = misc[5], nFr = misc[6], nK = misc[7];
 
-        // ---- fold: H += sum_f phi(k_f) v_f^T, s += sum_f phi(k_f) ----
-        for (int ft = wave; ft < F / 16; ft += NW) {
-            floatx4 acc[D / 16];
+        // ---- fold: H += sum phi(k) v^T, s += sum phi(k), 32 pairs at a time ----
+        for (int e0 = 0; e0 < nF; e0 += EC) {
+            const int ne = nF - e0 < EC ? nF - e0 : EC;
+            if (e0 > 0) __syncthreads();  // the previous chunk is consumed
+            if constexpr (BF) {
+                constexpr int EP = EC + 8;
+                uint16_t* P1 = (uint16_t*)(smem + sm.stage);  // [3][F][EP]
+                uint16_t* VTb = P1 + 3 * F * EP;             // [D][EP]
+                for (int idx = tid; idx < EC * (F / 4); idx += NT) {
+                    const int e1 = idx % EC, f4 = (idx / EC) * 4;
+                    float x[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (e1 < ne) load4(cand_phi(fold[e0 + e1]) + f4, x);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
+                    for (int k = 0; k < 4; ++k) {
+                        const uint16_t p1 = bf16_bits(x[k]);
+                        const float r1 = x[k] - bf16_val(p1);
+                        const uint16_t p2 = bf16_bits(r1);
+                        const uint16_t p3 = bf16_bits(r1 - bf16_val(p2));
+                        P1[(f4 + k) * EP + e1] = p1;
+                        P1[F * EP + (f4 + k) * EP + e1] = p2;
+                        P1[2 * F * EP + (f4 + k) * EP + e1] = p3;
+                    }
+                }
+                for (int idx = tid; idx < EC * (D / 8); idx += NT) {
+                    const int e1 = idx % EC, d8 = (idx / EC) * 8;
+                    uint4 t4 = make_uint4(0, 0, 0, 0);
+                    if (e1 < ne) t4 = *(const uint4*)(cand_v(fold[e0 + e1]) + d8);
+                    const uint32_t tw[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[dt][i] = Hs[(ft * 16 + qg * 4 + i) * HP + dt * 16 + r16];
-            for (int kk = 0; kk < nF; kk += 4) {
-                const int kx = kk + qg;
-                float av = 0.f;
-                const T* vr = nullptr;
-                if (kx < nF) {
-                    const int u = fold[kx];
-                    av = cand_phi(u)[ft * 16 + r16];
-                    vr = cand_v(u);
+                    for (int k = 0; k < 8; ++k) VTb[(d8 + k) * EP + e1] = (uint16_t)(tw[k >> 1] >> (16 * (k & 1)));
+                }
+                __syncthreads();
+                // s += phi^T 1: one feature tile per wave, B operand of ones (exact)
+                {
+                    const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80});
+                    for (int ft = wave; ft < FT; ft += NW) {
+                        floatx4 sa = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < EC / 32; ++ks) {
+                            const int o = (ft * 16 + r16) * EP + ks * 32 + qg * 8;
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + o), ones, sa, 0, 0, 0);
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + F * EP + o), ones, sa, 0, 0, 0);
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + 2 * F * EP + o), ones, sa, 0, 0, 0);
+                        }
+                        if (r16 == 0)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sP[perm_pos(ft * 16 + qg * 4 + i)] += sa[i];
+                    }
                 }
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    float bv = vr ? to_f32(vr[dt * 16 + r16]) : 0.f;
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[dt], 0, 0, 0);
+                for (int ks = 0; ks < EC / 32; ++ks) {
+                    const bf16x8 bv = *(const bf16x8*)(VTb + (wave * 16 + r16) * EP + ks * 32 + qg * 8);
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft) {
+                        const int o = (ft * 16 + r16) * EP + ks * 32 + qg * 8;
+                        Hr[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + o), bv, Hr[ft], 0, 0, 0);
+                        Hr[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + F * EP + o), bv, Hr[ft], 0, 0, 0);
+                        Hr[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(P1 + 2 * F * EP + o), bv, Hr[ft], 0,
+                                                                         0, 0);
+                    }
                 }
+            } else {
+                constexpr int EP = EC + 4;
+                float* PhT = (float*)(smem + sm.stage);  // [F][EP]
+                float* VTf = PhT + F * EP;               // [D][EP]
+                for (int idx = tid; idx < EC * (F / 4); idx += NT) {
+                    const int e1 = idx % EC, f4 = (idx / EC) * 4;
+                    float x[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (e1 < ne) load4(cand_phi(fold[e0 + e1]) + f4, x);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) PhT[(f4 + k) * EP + e1] = x[k];
+                }
+                for (int idx = tid; idx < EC * (D / 4); idx += NT) {
+                    const int e1 = idx % EC, d4 = (idx / EC) * 4;
+                    float x[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (e1 < ne) load4(cand_v(fold[e0 + e1]) + d4, x);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) VTf[(d4 + k) * EP + e1] = x[k];
+                }
+                __syncthreads();
+                for (int ft = wave; ft < FT; ft += NW) {
+                    floatx4 sa = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < EC / 4; ++kk)
+                        sa = __builtin_amdgcn_mfma_f32_16x16x4f32(PhT[(ft * 16 + r16) * EP + kk * 4 + qg], 1.0f, sa, 0, 0, 0);
+                    if (r16 == 0)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sP[perm_pos(ft * 16 + qg * 4 + i)] += sa[i];
+                }
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int kk = 0; kk < EC / 4; ++kk)
+                        Hr[ft] = __builtin_amdgcn_mfma_f32_16x16x4f32(PhT[(ft * 16 + r16) * EP + kk * 4 + qg],
+                                                                      VTf[(wave * 16 + r16) * EP + kk * 4 + qg], Hr[ft],
+                                                                      0, 0, 0);
             }
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Hs[(ft * 16 + qg * 4 + i) * HP + dt * 16 + r16] = acc[dt][i];
         }
-        for (int f = tid; f < F; f += 256) {
-            float acc = ss[f];
-            for (int kx = 0; kx < nF; ++kx) acc += cand_phi(fold[kx])[f];
-            ss[f] = acc;
-        }
-        __syncthreads();
 
-        // ---- kept leaving keys take the freed slots, then new slots ----
-        for (int i = tid; i < nK; i += 256) {
+        // ---- new bf16 parts of H; kept leaving keys take freed slots, then new slots ----
+        if (nF > 0) split_H();
+        for (int i = tid; i < nK; i += NT) {
             const int u = keptE[i];
             const int slot = i < nFr ? freed[i] : cnt + (i - nFr);
-            const int x = xE0 + (u - cnt);
-            cref[slot] = x;
-            cpos[slot] = upos[u];
-        }
-        for (int idx = tid; idx < nK * F; idx += 256) {
-            const int i = idx / F, f = idx % F;
-            const int u = keptE[i];
-            const int slot = i < nFr ? freed[i] : cnt + (i - nFr);
-            ws_cphi(a, chain, slot)[f] = ws_phiX(a, chain, xE0 + (u - cnt))[f];
+            cref[slot] = xE0 + (u - cnt);
+            cpos[slot] = (int)(eS + (u - cnt));
         }
         cnt = nU < C ? nU : C;
         __syncthreads();
     }
 
-    // ---- write the chain's state back ----
-    for (int i = tid; i < F * D; i += 256) ch.H()[i] = Hs[(i / D) * HP + (i % D)];
-    for (int i = tid; i < F; i += 256) ch.s()[i] = ss[i];
-    for (int i = tid; i < cnt; i += 256) ch.cpos()[i] = cpos[i];
-    for (int idx = tid; idx < cnt * D; idx += 256) {
+    // ---- state out ----
+    float* Hd = ch.H();
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+        *(float4*)(Hd + (size_t)(wave * 16 + r16) * F + ft * 16 + qg * 4) =
+            make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
+    for (int i = tid; i < F; i += NT) ch.s()[i] = sP[perm_pos(i)];
+    for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
+    for (int idx = tid; idx < cnt * D; idx += NT) {
         const int i = idx / D, j = idx % D;
         if (cref[i] >= 0) {
             ch.cache_k<T>()[(size_t)i * D + j] = xrow_k<T>(a, chain, b, g, cref[i])[j];
@@ -446,7 +741,7 @@ __global__ __launch_bounds__(256) void scan_kernel(Args a)
         const int64_t tend = t0 + n;
         const int64_t p0 = tend - w > t0 ? tend - w : t0;
         const int nr = (int)(tend - p0);
-        for (int idx = tid; idx < nr * D; idx += 256) {
+        for (int idx = tid; idx < nr * D; idx += NT) {
             const int i = idx / D, j = idx % D;
             const int64_t p = p0 + i;
             const int slot = (int)(p % w);
@@ -600,7 +895,7 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
         for (int mf = 0; mf < FM; ++mf) {
             float tmp[KPL];
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) tmp[j] = sH[(size_t)held_feature<Fh>(qg, mf * KPL + j) * D + dt * 16 + r16];
+            for (int j = 0; j < KPL; ++j) tmp[j] = sH[(size_t)(dt * 16 + r16) * F + held_feature<Fh>(qg, mf * KPL + j)];
             O[dt] = M::mma(M::pack(tmp), pf[mf], O[dt]);
         }
     }
