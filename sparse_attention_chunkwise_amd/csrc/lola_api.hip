@@ -5,6 +5,8 @@
 #include "lola_decode.h"
 #include "lola_internal.h"
 #include "lola_misc.h"
+#include "lola_output.h"
+#include "lola_decode_bf16.h"
 #include "lola_prefill.h"
 
 using namespace lola;
@@ -93,9 +95,15 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
     hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(scan_threads(D)), scan_lds, s, a);
     if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
-    const int wpi = (d.G * d.L + 63) / 64;
-    dim3 go(a.NI * wpi, chains);
-    hipLaunchKernelGGL((output_kernel<D, F, T>), go, dim3(256), 0, s, a);
+    if constexpr (sizeof(T) == 2) {
+        const int wpi = (d.G * d.L + kOutRows - 1) / kOutRows;
+        const size_t olds = out_smem(D, F, d.C).total;
+        if (allow_lds(output_kernel_bf16<D, F>, olds) != hipSuccess) return LOLA_ERR_HIP;
+        hipLaunchKernelGGL((output_kernel_bf16<D, F>), dim3(a.NI * wpi, chains), dim3(256), olds, s, a);
+    } else {
+        const int wpi = (d.G * d.L + 63) / 64;
+        hipLaunchKernelGGL((output_kernel<D, F, T>), dim3(a.NI * wpi, chains), dim3(256), 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess || mark(ev, 3, s) != hipSuccess) return LOLA_ERR_HIP;
     return LOLA_OK;
 }
@@ -103,9 +111,15 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
 template <int D, int F, typename T>
 lola_status launch_decode(Args& a, hipStream_t s)
 {
-    const size_t lds = decode_smem(D, F, a.d.G, a.d.C).total;
-    if (allow_lds(decode_kernel<D, F, T>, lds) != hipSuccess) return LOLA_ERR_HIP;
-    hipLaunchKernelGGL((decode_kernel<D, F, T>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+    if constexpr (sizeof(T) == 2) {
+        const size_t lds = dec_smem(D, F, a.d.C).total;
+        if (allow_lds(decode_kernel_bf16<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
+        hipLaunchKernelGGL((decode_kernel_bf16<D, F>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+    } else {
+        const size_t lds = decode_smem(D, F, a.d.G, a.d.C).total;
+        if (allow_lds(decode_kernel<D, F, T>, lds) != hipSuccess) return LOLA_ERR_HIP;
+        hipLaunchKernelGGL((decode_kernel<D, F, T>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+    }
     return hip_status(hipGetLastError());
 }
 
@@ -197,7 +211,7 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
     a.wl = ws_layout(d, batch, n_tokens);
     a.NI = a.wl.NI;
     if (workspace_bytes < a.wl.total) return LOLA_ERR_WORKSPACE;
-    if ((int64_t)a.NI * ((d.G * d.L + 63) / 64) > 0x7fffffff) return LOLA_ERR_UNSUPPORTED;
+    if ((int64_t)a.NI * ((d.G * d.L + 63) / 64) > 0x7fffffff) return LOLA_ERR_UNSUPPORTED;  // grid x
     a.ws = (unsigned char*)workspace;
     a.q = q;
     a.k = k;

@@ -1,0 +1,538 @@
+// Decode step for bf16 io (gfx950): one one-token update interval per
+// (sequence, KV head) chain, one workgroup (4 waves) per chain, state read and
+// written in place.
+//
+//   read   -- the chain's G query heads (MFMA columns) attend with exact
+//             softmax to the window [t-w+1, t] and the cache, streamed in
+//             blocks of 128 keys (32 per wave) with an online softmax per wave,
+//             merged at the end; the linear part is H^T phi(q) / s . phi(q)
+//             plus the key at t-w that leaves the window at this step (the new
+//             key itself when w = 0); one shared denominator (LoLA summary,
+//             "Inferentiestrategie", step 4).
+//   manage -- the SRE equation ("Het Self-Recall Error (SRE) Mechanisme") for
+//             every cached key and the leaving key against the step-start
+//             state, computed while their keys are staged for the read:
+//             phi(k) = [softmax(W k); softmax(-W k)] by MFMA with W in three
+//             bf16 parts, n^T = H^T phi^T with H and phi in bf16 hi/lo parts,
+//             d = phi . s; then the pair with the lowest SRE (newest on a tie)
+//             is folded into H, s by one outer product when the candidates
+//             exceed the capacity, and the leaving key takes its cache slot.
+#pragma once
+
+#include "lola_output.h"
+
+namespace lola {
+
+constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
+
+struct DecSmem {
+    size_t HhT, HlT, sP, cposL, esc, phiE, phiF, xrow, stK, stVT, misc, total;
+};
+
+__host__ __device__ inline DecSmem dec_smem(int D, int F, int C)
+{
+    DecSmem m;
+    const int Cp = C > 0 ? C : 1;
+    size_t off = 0;
+    m.HhT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
+    m.HlT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
+    m.sP = off;    off += align_up(sizeof(float) * F, 16);
+    m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
+    m.esc = off;   off += align_up(sizeof(float) * (size_t)(C + 1), 16);
+    m.phiE = off;  off += align_up(sizeof(float) * F, 16);
+    m.phiF = off;  off += align_up(sizeof(float) * F, 16);
+    m.xrow = off;  off += align_up(sizeof(float) * D, 16);
+    m.stK = off;   off += align_up(sizeof(uint16_t) * (size_t)kDecBlock * (D + 8), 16);
+    m.stVT = off;  off += align_up(sizeof(uint16_t) * (size_t)D * (kDecBlock + 8), 16);
+    m.misc = off;  off += sizeof(int) * 16;
+    m.total = align_up(off, 16);
+    return m;
+}
+
+// phi = [softmax(W x); softmax(-W x)] of one row by one wave in fp32 (lane i < Fh owns feature i)
+template <int D, int Fh>
+__device__ __forceinline__ void phi_row_wave(const float* W, const float* x, float* out, int lane)
+{
+    float z = 0.f;
+    if (lane < Fh)
+        for (int j = 0; j < D; ++j) z += W[(size_t)lane * D + j] * x[j];
+    const float zmax = wave_max(lane < Fh ? z : -INFINITY);
+    const float zmin = -wave_max(lane < Fh ? -z : -INFINITY);
+    const float ep = lane < Fh ? expf(z - zmax) : 0.f;
+    const float en = lane < Fh ? expf(zmin - z) : 0.f;
+    const float sp = wave_sum(ep), sn = wave_sum(en);
+    if (lane < Fh) { out[lane] = ep / sp; out[Fh + lane] = en / sn; }
+}
+
+template <int D, int F>
+__global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
+{
+    constexpr int NW = 4, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
+    constexpr int KBL = kDecBlock, KW = KBL / NW;  // keys per block, per wave
+    constexpr int HP = F + 8, KP = D + 8, VP = KBL + 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const Dims& d = a.d;
+    const int G = d.G, w = d.w, C = d.C;
+    const DecSmem sm = dec_smem(D, F, C);
+    uint16_t* HhT = (uint16_t*)(smem + sm.HhT);
+    uint16_t* HlT = (uint16_t*)(smem + sm.HlT);
+    float* sP = (float*)(smem + sm.sP);
+    int* cposL = (int*)(smem + sm.cposL);
+    float* esc = (float*)(smem + sm.esc);
+    float* phiE = (float*)(smem + sm.phiE);
+    float* phiF = (float*)(smem + sm.phiF);
+    float* xrow = (float*)(smem + sm.xrow);
+    uint16_t* stK = (uint16_t*)(smem + sm.stK);
+    uint16_t* stVT = (uint16_t*)(smem + sm.stVT);
+    int* misc = (int*)(smem + sm.misc);
+    float* mrg = (float*)(smem + sm.stK);  // merge area, reused after the key loop
+
+    const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    Chain ch = chain_of(a, chain);
+    const int64_t t = ch.tok();
+    const int cnt = min(max(ch.cnt(), 0), C);
+    const bf16* knew = (const bf16*)a.k + ((size_t)b * d.Hkv + g) * D;
+    const bf16* vnew = (const bf16*)a.v + ((size_t)b * d.Hkv + g) * D;
+    const bool hasE = (w == 0) || (t - w >= 0);
+    const int64_t pE = t - w;
+    const int rs = w > 0 ? (int)(t % w) : 0;
+    const bf16* kE = w == 0 ? knew : ch.ring_k<bf16>() + (size_t)rs * D;
+    const bf16* vE = w == 0 ? vnew : ch.ring_v<bf16>() + (size_t)rs * D;
+    const float* Wf = (const float*)(a.state + a.sl.W) + (size_t)g * Fh * D;
+    const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
+
+    // ---- state in: H^T hi/lo in operand order, s, cache positions ----
+    {
+        const float* Hst = ch.H();  // [D][F]
+        for (int i = tid; i < D * F / 4; i += 256) {
+            const int dd = (i * 4) / F, f = (i * 4) % F;
+            const float4 v4 = *(const float4*)(Hst + (size_t)dd * F + f);
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            uint16_t h[4], l[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                h[k] = bf16_bits(vv[k]);
+                l[k] = bf16_bits(vv[k] - bf16_val(h[k]));
+            }
+            const int o = dd * HP + perm_pos(f);  // four consecutive features stay consecutive
+            *(uint2*)(HhT + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            *(uint2*)(HlT + o) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        }
+        for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = ch.s()[i];
+        for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
+    }
+    // query frags (columns r16 < G), phi of the leaving key (wave 3, fp32)
+    bf16x8 qf[DS];
+    {
+        const bool qv = r16 < G;
+        const bf16* qp = (const bf16*)a.q + ((size_t)b * d.Hq + g * G + (qv ? r16 : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+            const uint4 u4 = qv ? *(const uint4*)(qp + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+            qf[ks] = __builtin_bit_cast(bf16x8, u4);
+        }
+    }
+    if (wave == NW - 1) {
+        for (int j = lane; j < D; j += 64) xrow[j] = hasE ? to_f32(kE[j]) : 0.f;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        phi_row_wave<D, Fh>(Wf, xrow, phiE, lane);
+    }
+    __syncthreads();
+
+    // ---- phi(q) for the query columns: z^T = W Q^T with W hi + lo ----
+    bf16x8 pf[FM];
+    float zl;
+    {
+        floatx4 zt[Fh / 16];
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft) {
+            zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + o), qf[ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + Fh * D + o), qf[ks], zt[ft], 0, 0, 0);
+            }
+        }
+        float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        float hv[F / 4];
+        float sp = 0.f, sn = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e1 = __expf(zt[ft][i] - zmax), e2 = __expf(zmin - zt[ft][i]);
+                hv[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+                hv[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+                sp += e1;
+                sn += e2;
+            }
+        sp += __shfl_xor(sp, 16, 64);
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 16, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float isp = 1.f / sp, isn = 1.f / sn;
+        float z = 0.f, kap = 0.f;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            u16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int hidx = mf * 8 + j;
+                const float x = hv[hidx] * (hidx < Fh / 4 ? isp : isn);
+                u[j] = bf16_bits(x);
+                const int pp = mf * 32 + qg * 8 + j;  // operand position of this feature
+                z += x * sP[pp];
+                // feature index of operand position pp for phi of the leaving key (natural order)
+                const int ftile = 2 * mf + (j >> 2), fidx = ftile * 16 + qg * 4 + (j & 3);
+                kap += x * phiE[fidx];
+            }
+            pf[mf] = __builtin_bit_cast(bf16x8, u);
+        }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        kap += __shfl_xor(kap, 16, 64);
+        kap += __shfl_xor(kap, 32, 64);
+        if (!hasE) kap = 0.f;
+        zl = z + kap;
+        // the leaving key's linear weight per query column, for the linear read of wave 0
+        if (wave == 0 && qg == 0) phiF[r16] = kap;
+    }
+    __syncthreads();
+
+    // ---- linear read (wave 0): O_lin^T = H^T phi(q)^T ----
+    floatx4 O[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun = 0.f, Zp = 0.f;
+    if (wave == 0) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int mf = 0; mf < FM; ++mf)
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(HhT + (dt * 16 + r16) * HP + mf * 32 + qg * 8),
+                                                                pf[mf], O[dt], 0, 0, 0);
+        // pending key: kappa * v_E, added to the linear part (weight e^-M, M floored at 0)
+        const float kap = phiF[r16];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            float vv[4];
+            if (hasE) load4(vE + dt * 16 + qg * 4, vv);
+            else vv[0] = vv[1] = vv[2] = vv[3] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[dt][i] += kap * vv[i];
+        }
+        Zp = qg == 0 ? zl : 0.f;
+    }
+
+    // ---- keys: window [ws0, t] then cache slots; blocks of 128, 32 per wave ----
+    const int64_t ws0 = t - w + 1 > 0 ? t - w + 1 : 0;
+    const int nWin = w > 0 ? (int)(t - ws0 + 1) : 0;
+    const int nK = nWin + cnt;
+    auto key_row = [&](int kidx, bool v) -> const bf16* {
+        if (kidx < nWin) {
+            const int64_t p = ws0 + kidx;
+            if (p == t) return v ? vnew : knew;
+            return (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)(p % w) * D;
+        }
+        return (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (size_t)(kidx - nWin) * D;
+    };
+    const float tau = d.tau;
+
+    // SRE of 16 candidates whose K^T frags are kb[] (column r16), values read by vfun(dt, i)
+    auto sre_tile = [&](const bf16x8* kb, bool colvalid, auto vfun) -> float {
+        floatx4 zt[Fh / 16];
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft) {
+            zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + o), kb[ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + Fh * D + o), kb[ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + 2 * Fh * D + o), kb[ks], zt[ft], 0, 0, 0);
+            }
+        }
+        float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        float hv[F / 4];
+        float sp = 0.f, sn = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e1 = expf(zt[ft][i] - zmax), e2 = expf(zmin - zt[ft][i]);
+                hv[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+                hv[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+                sp += e1;
+                sn += e2;
+            }
+        sp += __shfl_xor(sp, 16, 64);
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 16, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float isp = 1.f / sp, isn = 1.f / sn;
+        bf16x8 bh[FM], bl[FM];
+        float dd = 0.f;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            u16x8 uh, ul;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int hidx = mf * 8 + j;
+                const float x = hv[hidx] * (hidx < Fh / 4 ? isp : isn);
+                const uint16_t h = bf16_bits(x);
+                uh[j] = h;
+                ul[j] = bf16_bits(x - bf16_val(h));
+                dd += x * sP[mf * 32 + qg * 8 + j];
+            }
+            bh[mf] = __builtin_bit_cast(bf16x8, uh);
+            bl[mf] = __builtin_bit_cast(bf16x8, ul);
+        }
+        dd += __shfl_xor(dd, 16, 64);
+        dd += __shfl_xor(dd, 32, 64);
+        const float inv = dd > 0.f ? 1.f / dd : 0.f;
+        float e = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f}, acc2 = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mf = 0; mf < FM; ++mf) {
+                const int o = (dt * 16 + r16) * HP + mf * 32 + qg * 8;
+                const bf16x8 ah = *(const bf16x8*)(HhT + o);
+                const bf16x8 al = *(const bf16x8*)(HlT + o);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[mf], acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[mf], acc2, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[mf], acc2, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float df = (acc[i] + acc2[i]) * inv - (colvalid ? vfun(dt, i) : 0.f);
+                e += df * df;
+            }
+        }
+        e += __shfl_xor(e, 16, 64);
+        e += __shfl_xor(e, 32, 64);
+        return e;
+    };
+
+    const bool needSel = hasE && cnt + 1 > C;
+    const int nblk = (nK + KBL - 1) / KBL;
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int base = bi * KBL;
+        __syncthreads();  // previous block consumed
+        for (int idx = tid; idx < KBL * (D / 8); idx += 256) {
+            const int kr = idx / (D / 8), un = idx % (D / 8), kidx = base + kr;
+            const uint4 k4 = kidx < nK ? *(const uint4*)(key_row(kidx, false) + un * 8) : make_uint4(0, 0, 0, 0);
+            *(uint4*)(stK + kr * KP + un * 8) = k4;
+        }
+        for (int idx = tid; idx < (KBL / 2) * (D / 8); idx += 256) {
+            const int pr = idx / (D / 8), un = idx % (D / 8);
+            const int k0 = base + 2 * pr, k1 = k0 + 1;
+            const uint4 v0 = k0 < nK ? *(const uint4*)(key_row(k0, true) + un * 8) : make_uint4(0, 0, 0, 0);
+            const uint4 v1 = k1 < nK ? *(const uint4*)(key_row(k1, true) + un * 8) : make_uint4(0, 0, 0, 0);
+            const int kc = (2 * pr / KW) * KW + key_perm((2 * pr) % KW);
+            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                const uint32_t hi = (w1[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                *(uint32_t*)(stVT + (un * 8 + j) * VP + kc) = lo | (hi << 16);
+            }
+        }
+        __syncthreads();
+        // this wave's 32 keys: base + wave*32 + tt*16 + r16
+        const int kb0 = base + wave * KW;
+        if (kb0 >= nK) continue;
+        floatx4 sT[2];
+        bf16x8 kfr[2][DS];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            sT[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                kfr[tt][ks] = *(const bf16x8*)(stK + (wave * KW + tt * 16 + r16) * KP + ks * 32 + qg * 8);
+                sT[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[tt][ks], qf[ks], sT[tt], 0, 0, 0);
+            }
+        }
+        // online softmax for the query column r16 over the lane's 8 keys
+        {
+            float lg[8];
+            bool ok[8];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tt = j >> 2, i = j & 3;
+                const int kidx = kb0 + tt * 16 + qg * 4 + i;
+                ok[j] = kidx < nK && r16 < G;
+                lg[j] = tau * sT[tt][i];
+                if (ok[j]) bmax = fmaxf(bmax, lg[j]);
+            }
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+            const float mnew = fmaxf(mrun, bmax);
+            const float resc = __expf(mrun - mnew);
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) O[dt] *= resc;
+            Zp *= resc;
+            u16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float pv = ok[j] ? __expf(lg[j] - mnew) : 0.f;
+                Zp += pv;
+                u[j] = bf16_bits(pv);
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(stVT + (dt * 16 + r16) * VP + wave * KW + qg * 8),
+                                                                pb, O[dt], 0, 0, 0);
+        }
+        // SRE of the cached keys among the wave's 32 (only needed when a pair must be folded)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int k16 = kb0 + tt * 16;
+            if (!needSel || k16 + 15 < nWin || k16 >= nK) continue;  // wave-uniform
+            const int kidx = k16 + r16;
+            const bool cv = kidx >= nWin && kidx < nK;
+            const int kl = wave * KW + tt * 16 + r16;  // staged row
+            const int kc = (kl / KW) * KW + key_perm(kl % KW);
+            auto vfun = [&](int dt, int i) -> float { return bf16_val(stVT[(dt * 16 + qg * 4 + i) * VP + kc]); };
+            const float e = sre_tile(kfr[tt], cv, vfun);
+            if (qg == 0 && cv) esc[kidx - nWin] = e;
+        }
+    }
+
+    // ---- merge the waves' softmax parts, add the linear part, store ----
+    __syncthreads();  // staging area becomes the merge area
+    {
+        float* mM = mrg;                 // [NW][16]
+        float* mZ = mrg + NW * 16;       // [NW][16]
+        float* mO = mrg + 2 * NW * 16;   // [NW][D][16]
+        float Z = Zp;
+        Z += __shfl_xor(Z, 16, 64);
+        Z += __shfl_xor(Z, 32, 64);
+        if (qg == 0) { mM[wave * 16 + r16] = mrun; mZ[wave * 16 + r16] = Z; }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mO[(wave * D + dt * 16 + qg * 4 + i) * 16 + r16] = O[dt][i];
+        __syncthreads();
+        for (int idx = tid; idx < G * D; idx += 256) {
+            const int col = idx / D, dd = idx % D;
+            float M = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mM[ww * 16 + col]);
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float sc = __expf(mM[ww * 16 + col] - M);
+                num += sc * mO[(ww * D + dd) * 16 + col];
+                den += sc * mZ[ww * 16 + col];
+            }
+            ((bf16*)a.out)[((size_t)b * d.Hq + g * G + col) * D + dd] = from_f32<bf16>(num / den);
+        }
+    }
+
+    // ---- SRE of the leaving key (wave 0), then the pair to fold ----
+    const int nU = cnt + (hasE ? 1 : 0);
+    if (hasE && nU > C && wave == 0) {
+        bf16x8 kb[DS];
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+            const uint4 u4 = r16 == 0 ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+            kb[ks] = __builtin_bit_cast(bf16x8, u4);
+        }
+        float vreg[DT * 4];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) load4(vE + dt * 16 + qg * 4, vreg + dt * 4);
+        auto vfun = [&](int dt, int i) -> float { return vreg[dt * 4 + i]; };
+        const float e = sre_tile(kb, r16 == 0, vfun);
+        if (lane == 0) esc[cnt] = e;
+    }
+    __syncthreads();
+    int victim = -1;
+    if (hasE && nU > C) {
+        if (wave == 0) {
+            // lowest SRE, newest position on a tie: minimise (bits(e), ~pos)
+            unsigned long long best = ~0ull;
+            for (int u = lane; u < nU; u += 64) {
+                const uint32_t pos = u < cnt ? (uint32_t)cposL[u] : (uint32_t)pE;
+                const unsigned long long key = ((unsigned long long)__float_as_uint(esc[u]) << 32) | (0xffffffffu - pos);
+                best = key < best ? key : best;
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                const unsigned long long other = __shfl_xor(best, o, 64);
+                best = other < best ? other : best;
+            }
+            const uint32_t pos = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
+            int vi = cnt;
+            for (int u = lane; u < cnt; u += 64)
+                if ((uint32_t)cposL[u] == pos) vi = u;
+            for (int o = 32; o > 0; o >>= 1) vi = min(vi, __shfl_xor(vi, o, 64));
+            if (lane == 0) misc[0] = vi;
+        }
+        __syncthreads();
+        victim = misc[0];
+        // phi of the folded key in fp32 (wave 0), then H += phi v^T, s += phi
+        if (wave == 0) {
+            const bf16* kr = victim < cnt ? ch.cache_k<bf16>() + (size_t)victim * D : kE;
+            for (int j = lane; j < D; j += 64) xrow[j] = to_f32(kr[j]);
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            phi_row_wave<D, Fh>(Wf, xrow, phiF, lane);
+        }
+        __syncthreads();
+        const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
+        float* Hd = ch.H();
+        for (int i = tid; i < D * F; i += 256) {
+            const int dd = i / F, f = i % F;
+            Hd[i] += to_f32(vr[dd]) * phiF[f];
+        }
+        for (int f = tid; f < F; f += 256) ch.s()[f] += phiF[f];
+    }
+    __syncthreads();
+
+    // ---- cache slot, then the ring (the leaving pair lives in slot t % w) ----
+    int slot = -1;
+    if (hasE) {
+        if (nU <= C) slot = cnt;
+        else if (victim < cnt) slot = victim;
+    }
+    if (slot >= 0)
+        for (int j = tid; j < D; j += 256) {
+            ch.cache_k<bf16>()[(size_t)slot * D + j] = kE[j];
+            ch.cache_v<bf16>()[(size_t)slot * D + j] = vE[j];
+        }
+    __syncthreads();
+    if (w > 0)
+        for (int j = tid; j < D; j += 256) {
+            ch.ring_k<bf16>()[(size_t)rs * D + j] = knew[j];
+            ch.ring_v<bf16>()[(size_t)rs * D + j] = vnew[j];
+        }
+    if (tid == 0) {
+        if (slot >= 0) ch.cpos()[slot] = (int32_t)pE;
+        if (hasE && nU <= C) ch.cnt() = cnt + 1;
+        ch.tok() = t + 1;
+    }
+}
+
+}  // namespace lola

@@ -38,14 +38,14 @@ struct StateHeader {
     int32_t pad[3];
 };
 
-// State buffer: header | W [Hkv][Fh][D] f32 | chains [B][Hkv]
+// State buffer: header | W [Hkv][Fh][D] f32 | Wb [Hkv][3][Fh][D] bf16 (three parts of W, largest first) | chains [B][Hkv]
 // chain: tokens seen i64 | cache_count i32 | H^T [D][F] f32 | s [F] f32 | cache_pos [C] i32 |
 //        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io
 // Every chain keeps its own token count so that concurrent chains of one
 // sequence never race on a shared counter.  The window ring slot of
 // position p is p % w.
 struct StateLayout {
-    size_t W, chains, chain_bytes;
+    size_t W, Wb, chains, chain_bytes;
     size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v;
     size_t total;
 };
@@ -56,6 +56,8 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     size_t off = 256;
     s.W = off;
     off = align_up(off + sizeof(float) * (size_t)d.Hkv * d.Fh * d.D, 256);
+    s.Wb = off;
+    off = align_up(off + sizeof(uint16_t) * 3 * (size_t)d.Hkv * d.Fh * d.D, 256);
     s.chains = off;
     size_t c = 0;
     s.otok = 0;
@@ -78,7 +80,8 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 //   cache0_k/v [B][Hkv][C][D] io | cphi [B][Hkv][C][F] f32 |
 //   phiS [B][Hkv][X][2F] bf16 | cphiS [B][Hkv][C][2F] bf16 (hi then lo parts of
 //   phi, features in the SRE operand order) |
-//   snapH [B][Hkv][NI][D][F] f32 (H^T) | snapS [B][Hkv][NI][F] f32 |
+//   snapH [B][Hkv][NI][D][F] H^T: f32 for f32 io; bf16 in operand order for bf16 io |
+//   snapS [B][Hkv][NI][F] f32 |
 //   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32
 struct WsLayout {
     size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, snapH, snapS, snapRef, snapN;

@@ -19,7 +19,19 @@ __global__ __launch_bounds__(256) void init_kernel(Args a, const float* W, uint6
         }
         float* Wd = (float*)(a.state + a.sl.W);
         const size_t nw = (size_t)a.d.Hkv * a.d.Fh * a.d.D;
-        for (size_t i = threadIdx.x; i < nw; i += 256) Wd[i] = W[i];
+        uint16_t* Wb = (uint16_t*)(a.state + a.sl.Wb);
+        const size_t per = (size_t)a.d.Fh * a.d.D;
+        for (size_t i = threadIdx.x; i < nw; i += 256) {
+            const float x = W[i];
+            Wd[i] = x;
+            const uint16_t h = __builtin_bit_cast(uint16_t, (__bf16)x);
+            const float r1 = x - __uint_as_float((uint32_t)h << 16);
+            const uint16_t m = __builtin_bit_cast(uint16_t, (__bf16)r1);
+            const size_t gi = i / per, r = i % per;
+            Wb[(3 * gi) * per + r] = h;
+            Wb[(3 * gi + 1) * per + r] = m;
+            Wb[(3 * gi + 2) * per + r] = __builtin_bit_cast(uint16_t, (__bf16)(r1 - __uint_as_float((uint32_t)m << 16)));
+        }
         return;
     }
     uint32_t* p = (uint32_t*)(a.state + a.sl.chains + (size_t)blk * a.sl.chain_bytes);

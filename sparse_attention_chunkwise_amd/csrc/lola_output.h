@@ -1,0 +1,353 @@
+// Output pass for bf16 io (gfx950), LDS-staged.
+//
+// One workgroup (4 waves) handles 128 query rows of one (interval, chain);
+// each wave owns 32 rows as two 16-column MFMA tiles (the queries are the
+// columns, so softmax statistics live in the lanes).  Per workgroup:
+//   - H_c^T (bf16, features in operand order) and W (bf16 hi + lo) staged once;
+//   - z^T = W Q^T gives phi(q) (two softmax halves over the features),
+//     O^T = H_c^T phi(q)^T and Z = s_c . phi(q) start the accumulators
+//     (linear read of the interval-start state, LoLA summary section
+//     "Inferentiestrategie", step 4);
+//   - keys in blocks of 32 (the window span of the interval, then the cache
+//     snapshot): K, V^T and phi(K) are staged in LDS with 16-byte loads, the
+//     next block prefetched into registers; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
+//     for keys that left the window inside the interval, online softmax with
+//     a running max floored at 0 so the linear terms carry e^-M, and
+//     O^T += V^T P^T;
+//   - o = O / Z with one shared denominator.
+#pragma once
+
+#include "lola_prefill.h"
+
+namespace lola {
+
+constexpr int kOutRows = 128;  // query rows per workgroup
+constexpr int kKeyBlock = 32;
+
+struct OutSmem {
+    size_t sP, refs, Ks, VT, Pk, total;
+};
+
+__host__ __device__ inline OutSmem out_smem(int D, int F, int C)
+{
+    OutSmem m;
+    size_t off = 0;
+    m.sP = off;   off += align_up(sizeof(float) * F, 16);
+    m.refs = off; off += align_up(sizeof(int) * (size_t)(C > 0 ? C : 1), 16);
+    m.Ks = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (D + 8);
+    m.VT = off;   off += sizeof(uint16_t) * (size_t)D * (kKeyBlock + 8);
+    m.Pk = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (F + 8);
+    m.total = align_up(off, 16);
+    return m;
+}
+
+// position of key k (0..31) of a block in the P^T / V^T operand order
+__device__ __forceinline__ int key_perm(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
+
+template <int D, int F>
+__global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Args a)
+{
+    constexpr int NW = 4, RT = 2, KB = kKeyBlock, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
+    constexpr int KP = D + 8, VP = KB + 8, PP = F + 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const Dims& d = a.d;
+    const OutSmem sm = out_smem(D, F, d.C);
+    float* sP = (float*)(smem + sm.sP);
+    int* srefL = (int*)(smem + sm.refs);
+    uint16_t* Ks = (uint16_t*)(smem + sm.Ks);
+    uint16_t* VT = (uint16_t*)(smem + sm.VT);
+    uint16_t* Pk = (uint16_t*)(smem + sm.Pk);
+
+    const int G = d.G, L = d.L, w = d.w;
+    const int chain = blockIdx.y, b = chain / d.Hkv, g = chain % d.Hkv;
+    const int rows = G * L;
+    const int wpi = (rows + kOutRows - 1) / kOutRows;
+    const int c = blockIdx.x / wpi, rblk = blockIdx.x % wpi;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    const int NI = a.NI;
+    const int64_t t0 = ws_t0(a, b);
+    const int64_t ap = t0 + (int64_t)c * L;
+    const int64_t ep = ap + L < t0 + a.n ? ap + L : t0 + a.n;
+    const int Lc = (int)(ep - ap);
+
+    // ---- stage s_c (operand order) and the cache refs of the snapshot ----
+    const uint16_t* HTg = (const uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D;  // [D][F] bf16
+    const uint16_t* Whg = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;          // [Fh][D]
+    const uint16_t* Wlg = Whg + (size_t)Fh * D;
+    {
+        const float* sS = (const float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
+        for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = sS[i];
+        const int Cp0 = d.C > 0 ? d.C : 1;
+        const int cc0 = ((const int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c];
+        const int* sr0 = (const int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp0;
+        for (int i = tid; i < cc0; i += 256) srefL[i] = sr0[i];
+    }
+
+    // ---- this lane's queries (columns r16 of the wave's two row tiles) ----
+    int64_t tq[RT];
+    int hq_[RT];
+    bool qv[RT];
+    bf16x8 qf[RT][DS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = rblk * kOutRows + wave * 32 + rt * 16 + r16;
+        const int hl = r / L, ti = r % L;
+        qv[rt] = r < rows && ti < Lc;
+        hq_[rt] = g * G + (qv[rt] ? hl : 0);
+        tq[rt] = qv[rt] ? ap + ti : -1;
+        const bf16* qp = (const bf16*)a.q + (((size_t)b * a.n + (size_t)(qv[rt] ? ap + ti - t0 : 0)) * d.Hq + hq_[rt]) * D;
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+            const uint4 u4 = qv[rt] ? *(const uint4*)(qp + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+            qf[rt][ks] = __builtin_bit_cast(bf16x8, u4);
+        }
+    }
+    __syncthreads();
+
+    // ---- phi(q): z^T = W Q^T (W hi + lo), two softmax halves per query ----
+    bf16x8 pf[RT][FM];
+    float zl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        floatx4 zt[Fh / 16];
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft) {
+            zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Whg + o), qf[rt][ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wlg + o), qf[rt][ks], zt[ft], 0, 0, 0);
+            }
+        }
+        float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        float ph[Fh / 4], pn[Fh / 4];
+        float sp = 0.f, sn = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ph[ft * 4 + i] = __expf(zt[ft][i] - zmax);
+                pn[ft * 4 + i] = __expf(zmin - zt[ft][i]);
+                sp += ph[ft * 4 + i];
+                sn += pn[ft * 4 + i];
+            }
+        sp += __shfl_xor(sp, 16, 64);
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 16, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float isp = 1.f / sp, isn = 1.f / sn;
+        // operand order: step mf covers feature tiles 2mf, 2mf+1; features ft*16+qg*4+i
+        float hv[F / 4];
+#pragma unroll
+        for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hv[(ft >> 1) * 8 + (ft & 1) * 4 + i] = ph[ft * 4 + i] * isp;                 // feature ft*16+qg*4+i
+                hv[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = pn[ft * 4 + i] * isn;        // feature Fh+ft*16+...
+            }
+        float z = 0.f;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            u16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                u[j] = bf16_bits(hv[mf * 8 + j]);
+                z += hv[mf * 8 + j] * sP[mf * 32 + qg * 8 + j];
+            }
+            pf[rt][mf] = __builtin_bit_cast(bf16x8, u);
+        }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        zl[rt] = z;
+    }
+
+    // ---- linear read of the snapshot state: O^T = H_c^T phi(q)^T ----
+    floatx4 O[RT][DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) O[rt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            const bf16x8 ha = *(const bf16x8*)(HTg + (size_t)(dt * 16 + r16) * F + mf * 32 + qg * 8);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pf[rt][mf], O[rt][dt], 0, 0, 0);
+        }
+    }
+    float Zp[RT], mrun[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) { Zp[rt] = qg == 0 ? zl[rt] : 0.f; mrun[rt] = 0.f; }
+
+    // ---- keys: window span [sp0, ep) then the snapshot cache ----
+    const int Cp = d.C > 0 ? d.C : 1;
+    const int64_t sp0 = ap - w > 0 ? ap - w : 0;
+    const int nSpan = (int)(ep - sp0);
+    const int ccnt = ((const int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c];
+    const int* sref = srefL;
+    const int nK = nSpan + ccnt;
+    const int xs0 = (int)(sp0 - (t0 - w));
+    const float tau = d.tau;
+    const int64_t lastPend = ep - 1 - w;
+    constexpr int KU = KB * D / 8 / 256;   // 16-byte units per thread for K (and V)
+    constexpr int PU = KB * F / 8 / 256;   // for phi(K)
+    constexpr int VPU = (KB / 2) * (D / 8);  // (key pair, 8-value unit) items for V
+    static_assert(VPU <= 256, "one V key-pair unit per thread at most");
+    uint4 pk[KU], pv[2], pp[PU];
+#define LOLA_OUT_PREFETCH(BASE)                                                                                      \
+    do {                                                                                                             \
+        _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
+            const int idx = tid + k * 256, kr = idx / (D / 8), un = idx % (D / 8);                                   \
+            const int kidx = (BASE) + kr, kc = kidx < nK ? kidx : 0;                                                 \
+            const bf16* kp = kc < nSpan ? xrow_k<bf16>(a, chain, b, g, xs0 + kc) : ref_k<bf16>(a, chain, b, g, sref[kc - nSpan]); \
+            const uint4 k4 = *(const uint4*)(kp + un * 8);                                                           \
+            pk[k] = kidx < nK ? k4 : make_uint4(0, 0, 0, 0);                                                         \
+        }                                                                                                            \
+        if (tid < VPU) {                                                                                             \
+            const int pr = tid / (D / 8), un = tid % (D / 8);                                                        \
+            _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
+                const int kidx = (BASE) + 2 * pr + k, kc = kidx < nK ? kidx : 0;                                     \
+                const bf16* vp = kc < nSpan ? xrow_v<bf16>(a, chain, b, g, xs0 + kc) : ref_v<bf16>(a, chain, b, g, sref[kc - nSpan]); \
+                const uint4 v4 = *(const uint4*)(vp + un * 8);                                                       \
+                pv[k] = kidx < nK ? v4 : make_uint4(0, 0, 0, 0);                                                     \
+            }                                                                                                        \
+        }                                                                                                            \
+        _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
+            const int idx = tid + k * 256, kr = idx / (F / 8), un = idx % (F / 8), kidx = (BASE) + kr;               \
+            const bool want = kidx < nSpan && sp0 + kidx <= lastPend;                                                \
+            const uint4 p4 = *(const uint4*)(ws_phiS(a, chain, xs0 + (want ? kidx : 0)) + un * 8);                   \
+            pp[k] = want ? p4 : make_uint4(0, 0, 0, 0);                                                              \
+        }                                                                                                            \
+    } while (0)
+    if (nK > 0) LOLA_OUT_PREFETCH(0);
+    for (int base = 0; base < nK; base += KB) {
+        __syncthreads();  // the previous block (or W) is no longer read
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int idx = tid + k * 256, kr = idx / (D / 8), un = idx % (D / 8);
+            *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
+        }
+        if (tid < VPU) {
+            // keys 2pr, 2pr+1 sit next to each other in the operand order
+            const int pr = tid / (D / 8), un = tid % (D / 8), kc = key_perm(2 * pr);
+            const uint32_t w0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w}, w1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                const uint32_t hi = (w1[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                *(uint32_t*)(VT + (un * 8 + j) * VP + kc) = lo | (hi << 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PU; ++k) {
+            const int idx = tid + k * 256, kr = idx / (F / 8), un = idx % (F / 8);
+            *(uint4*)(Pk + kr * PP + un * 8) = pp[k];
+        }
+        __syncthreads();
+        if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB);
+        const bool anyPend = base < nSpan && sp0 + base <= lastPend;
+
+        floatx4 sT[RT][2], kT[RT][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = kT[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                const bf16x8 ka = *(const bf16x8*)(Ks + (tt * 16 + r16) * KP + ks * 32 + qg * 8);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rt][ks], sT[rt][tt], 0, 0, 0);
+            }
+            if (anyPend) {
+#pragma unroll
+                for (int mf = 0; mf < FM; ++mf) {
+                    const bf16x8 pa = *(const bf16x8*)(Pk + (tt * 16 + r16) * PP + mf * 32 + qg * 8);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) kT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, pf[rt][mf], kT[rt][tt], 0, 0, 0);
+                }
+            }
+        }
+        bf16x8 pb[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            // the lane's 8 keys: base + tt*16 + qg*4 + i, operand slot j = tt*4 + i
+            float lg[8];
+            int kind[8];
+            float bmax = -INFINITY;
+            // query position relative to the span start; span key kidx sits at sp0 + kidx
+            const int tr = qv[rt] ? (int)(tq[rt] - sp0) : -1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tt = j >> 2, i = j & 3;
+                const int kidx = base + tt * 16 + qg * 4 + i;
+                int kd = 0;
+                if (tr >= 0 && kidx < nK) {
+                    if (kidx < nSpan) {
+                        if (kidx <= tr) kd = (kidx >= tr - w + 1) ? 1 : 2;
+                    } else {
+                        kd = 1;
+                    }
+                }
+                kind[j] = kd;
+                lg[j] = tau * sT[rt][tt][i];
+                if (kd == 1) bmax = fmaxf(bmax, lg[j]);
+            }
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+            const float mnew = fmaxf(mrun[rt], bmax);
+            const float resc = __expf(mrun[rt] - mnew);
+            mrun[rt] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
+            Zp[rt] *= resc;
+            const float elin = __expf(-mnew);
+            u16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tt = j >> 2, i = j & 3;
+                float pv_ = 0.f;
+                if (kind[j] == 1) pv_ = __expf(lg[j] - mnew);
+                else if (kind[j] == 2) pv_ = kT[rt][tt][i] * elin;
+                Zp[rt] += pv_;
+                u[j] = bf16_bits(pv_);
+            }
+            pb[rt] = __builtin_bit_cast(bf16x8, u);
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + qg * 8);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], O[rt][dt], 0, 0, 0);
+        }
+    }
+
+#undef LOLA_OUT_PREFETCH
+    // ---- shared denominator, store o[t][h][d] ----
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float Z = Zp[rt];
+        Z += __shfl_xor(Z, 16, 64);
+        Z += __shfl_xor(Z, 32, 64);
+        if (qv[rt]) {
+            bf16* op = (bf16*)a.out + (((size_t)b * a.n + (size_t)(tq[rt] - t0)) * d.Hq + hq_[rt]) * D;
+            const float inv = 1.f / Z;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t lo = (uint32_t)bf16_bits(O[rt][dt][0] * inv) | ((uint32_t)bf16_bits(O[rt][dt][1] * inv) << 16);
+                const uint32_t hi = (uint32_t)bf16_bits(O[rt][dt][2] * inv) | ((uint32_t)bf16_bits(O[rt][dt][3] * inv) << 16);
+                *(uint2*)(op + dt * 16 + qg * 4) = make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
+}  // namespace lola

@@ -230,7 +230,7 @@ constexpr int kFoldChunk = 64;  // folded pairs staged per fold chunk
 __host__ __device__ constexpr int scan_threads(int D) { return 4 * D; }  // D/16 waves
 
 struct ScanSmem {
-    size_t stage, part, ebits, keep, fold, memb, freed, keptE, cref, cpos, hist, s, dS, misc, total;
+    size_t stage, part, ebits, keep, fold, memb, freed, keptE, cref, cpos, hist, s, dS, ucode, bcnt, misc, total;
     int sphi_stride, sv_stride;  // elements per staged phi row (bf16) / value row
 };
 
@@ -257,6 +257,8 @@ __host__ __device__ inline ScanSmem scan_smem(int D, int F, int C, int L, int es
     m.hist = off;  off += sizeof(int) * kSelBins;
     m.s = off;     off += sizeof(float) * F;
     m.dS = off;    off += sizeof(float) * kBatch;
+    m.ucode = off; off += sizeof(int) * U;
+    m.bcnt = off;  off += sizeof(int) * 4 * ((U + 63) / 64);
     m.misc = off;  off += sizeof(int) * 16;
     m.total = align_up(off, 16);
     return m;
@@ -322,6 +324,8 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     int* hist = (int*)(smem + sm.hist);
     float* sP = (float*)(smem + sm.s);  // s in operand (perm_pos) order
     float* dS = (float*)(smem + sm.dS);
+    int* ucode = (int*)(smem + sm.ucode);  // candidate source: X row (>= 0) or call-start cache slot -code-1
+    int* bcnt = (int*)(smem + sm.bcnt);
     int* misc = (int*)(smem + sm.misc);
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
@@ -376,10 +380,18 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
 
         // ---- interval-start snapshot (H^T [D][F], s, cache refs) ----
         {
-            float* dst = snapH + (size_t)c * F * D + (size_t)(wave * 16 + r16) * F + qg * 4;
+            if constexpr (BF) {
+                // the hi parts are exactly the SRE operand: features in operand order
+                uint16_t* dst = (uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D +
+                                (size_t)(wave * 16 + r16) * F + qg * 8;
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft)
-                *(float4*)(dst + ft * 16) = make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
+                for (int m = 0; m < FM; ++m) *(bf16x8*)(dst + m * 32) = Ah[m];
+            } else {
+                float* dst = snapH + (size_t)c * F * D + (size_t)(wave * 16 + r16) * F + qg * 4;
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+                    *(float4*)(dst + ft * 16) = make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
+            }
             for (int i = tid; i < F; i += NT) snapS[(size_t)c * F + i] = sP[perm_pos(i)];
             for (int i = tid; i < cnt; i += NT) snapRef[(size_t)c * Cp + i] = cref[i];
             if (tid == 0) snapN[c] = cnt;
@@ -391,20 +403,30 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         const int nE = eE > eS ? (int)(eE - eS) : 0;
         const int nU = cnt + nE;
         const int xE0 = (int)(eS - (t0 - w));
-        auto cand_phi = [&](int u) -> const float* {
-            if (u >= cnt) return ws_phiX(a, chain, xE0 + (u - cnt));
-            const int r = cref[u];
-            return r >= 0 ? ws_phiX(a, chain, r) : ws_cphi(a, chain, -r - 1);
+        for (int u = tid; u < nU; u += NT) ucode[u] = u < cnt ? cref[u] : xE0 + (u - cnt);
+        const float* phiX0 = ws_phiX(a, chain, 0);
+        const float* cphi0 = ws_cphi(a, chain, 0);
+        const uint16_t* phiS0 = ws_phiS(a, chain, 0);
+        const uint16_t* cphiS0 = ws_cphiS(a, chain, 0);
+        const T* vin0 = (const T*)a.v + ((size_t)b * n * d.Hkv + g) * D;   // + (x - w) * Hkv * D
+        const T* ring0v = (const T*)(a.ws + a.wl.ring0_v) + (size_t)chain * w * D;
+        const T* cache0v = (const T*)(a.ws + a.wl.cache0_v) + (size_t)chain * Cp * D;
+        auto code_phi = [&](int code) -> const float* {
+            return code >= 0 ? phiX0 + (size_t)code * F : cphi0 + (size_t)(-code - 1) * F;
         };
-        auto cand_phs = [&](int u) -> const uint16_t* {
-            if (u >= cnt) return ws_phiS(a, chain, xE0 + (u - cnt));
-            const int r = cref[u];
-            return r >= 0 ? ws_phiS(a, chain, r) : ws_cphiS(a, chain, -r - 1);
+        auto code_phs = [&](int code) -> const uint16_t* {
+            return code >= 0 ? phiS0 + (size_t)code * 2 * F : cphiS0 + (size_t)(-code - 1) * 2 * F;
         };
-        auto cand_v = [&](int u) -> const T* {
-            return u < cnt ? ref_v<T>(a, chain, b, g, cref[u]) : xrow_v<T>(a, chain, b, g, xE0 + (u - cnt));
+        auto code_v = [&](int code) -> const T* {
+            const T* pin = vin0 + (size_t)(code - w) * d.Hkv * D;
+            const T* pring = ring0v + (size_t)code * D;
+            const T* pcache = cache0v + (size_t)(-code - 1) * D;
+            return code >= w ? pin : (code >= 0 ? pring : pcache);
         };
+        auto cand_phi = [&](int u) -> const float* { return code_phi(ucode[u]); };
+        auto cand_v = [&](int u) -> const T* { return code_v(ucode[u]); };
         auto cand_pos = [&](int u) -> int { return u < cnt ? cpos[u] : (int)(eS + (u - cnt)); };
+        __syncthreads();  // codes ready
 
         // ---- SRE in batches of 64 candidates ----
         const int nbat = (nU + BATCH - 1) / BATCH;
@@ -414,15 +436,17 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
             for (int k = 0; k < PU_PT; ++k) {
                 const int idx = tid + k * NT;
                 const int cl = idx / PU_ROW, un = idx % PU_ROW, u = bi * BATCH + cl;
-                pre_p[k] = (idx < BATCH * PU_ROW && u < nU) ? *(const uint4*)(cand_phs(u) + un * 8)
-                                                            : make_uint4(0, 0, 0, 0);
+                const bool ok = idx < BATCH * PU_ROW && u < nU;
+                const uint4 t4 = *(const uint4*)(code_phs(ucode[ok ? u : 0]) + un * 8);
+                pre_p[k] = ok ? t4 : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int k = 0; k < VU_PT; ++k) {
                 const int idx = tid + k * NT;
                 const int cl = idx / VU_ROW, un = idx % VU_ROW, u = bi * BATCH + cl;
-                pre_v[k] = (idx < BATCH * VU_ROW && u < nU) ? *(const uint4*)(cand_v(u) + un * VU)
-                                                            : make_uint4(0, 0, 0, 0);
+                const bool ok = idx < BATCH * VU_ROW && u < nU;
+                const uint4 t4 = *(const uint4*)(code_v(ucode[ok ? u : 0]) + un * VU);
+                pre_v[k] = ok ? t4 : make_uint4(0, 0, 0, 0);
             }
         };
         if (nbat > 0) prefetch(0);
@@ -509,104 +533,117 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
                 }
             }
         }
-        __syncthreads();
-        for (int u = tid; u < nU; u += NT) {
-            float e = part[u];
+        __syncthreads();  // per-wave partial errors complete
+
+        // ---- SRE totals and exact top-C on (SRE desc, position asc), all waves ----
+        {
+            uint32_t lo = 0xffffffffu, hi = 0u;
+            for (int u = tid; u < nU; u += NT) {
+                float e = part[u];
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) e += part[ww * U + u];
-            ebits[u] = __float_as_uint(e);
+                for (int ww = 1; ww < NW; ++ww) e += part[ww * U + u];
+                const uint32_t eb = __float_as_uint(e);
+                ebits[u] = eb;
+                lo = min(lo, eb);
+                hi = max(hi, eb);
+            }
+            lo = wave_min_u32(lo);
+            hi = wave_max_u32(hi);
+            if (tid == 0) { misc[0] = (int)lo; misc[1] = (int)hi; misc[2] = 0; }
+            for (int i = tid; i < NB; i += NT) hist[i] = 0;
+            __syncthreads();
+            if (lane == 0 && wave > 0) { atomicMin((uint32_t*)&misc[0], lo); atomicMax((uint32_t*)&misc[1], hi); }
+        }
+        __syncthreads();
+        if (nU > C && C > 0) {
+            const uint32_t minb = (uint32_t)misc[0];
+            // monotone bin of an SRE bit pattern (same formula in every pass)
+            const float bscale = (float)NB / ((float)((uint32_t)misc[1] - minb) + 1.0f);
+            auto bin_of = [&](uint32_t x) { return min(NB - 1, (int)((float)(x - minb) * bscale)); };
+            for (int u = tid; u < nU; u += NT) atomicAdd(&hist[bin_of(ebits[u])], 1);
+            __syncthreads();
+            // every wave scans the bins (highest first; lane l holds bins NB-1-4l .. NB-4-4l)
+            int cb[4], tot = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { cb[k] = hist[NB - 1 - (4 * lane + k)]; tot += cb[k]; }
+            int incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int up = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += up;
+            }
+            const int excl = incl - tot;
+            int bsel = -1, above = 0;
+            if (excl < C && incl >= C) {
+                int cum = excl;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (bsel < 0 && cum + cb[k] >= C) { bsel = NB - 1 - (4 * lane + k); above = cum; }
+                    cum += cb[k];
+                }
+            }
+            const uint64_t hit = __ballot(bsel >= 0);
+            const int src = __ffsll((long long)hit) - 1;
+            const int bstar = __shfl(bsel, src, 64);
+            const int need = C - __shfl(above, src, 64);
+            for (int u = tid; u < nU; u += NT) {
+                const int bin = bin_of(ebits[u]);
+                if (bin != bstar) keep[u] = bin > bstar;
+                else memb[atomicAdd(&misc[2], 1)] = u;
+            }
+            __syncthreads();
+            const int m = misc[2];
+            for (int i = tid; i < m; i += NT) {
+                const int u = memb[i];
+                const uint32_t eu = ebits[u];
+                const int pu = cand_pos(u);
+                int rank = 0;
+                for (int j2 = 0; j2 < m; ++j2) {
+                    const int v2 = memb[j2];
+                    const uint32_t ev = ebits[v2];
+                    rank += (ev > eu) || (ev == eu && cand_pos(v2) < pu);
+                }
+                keep[u] = rank < need;
+            }
+        } else {
+            for (int u = tid; u < nU; u += NT) keep[u] = nU <= C;
         }
         __syncthreads();
 
-        // ---- exact top-C on (SRE desc, position asc), then compaction: wave 0 ----
-        if (wave == 0) {
+        // ---- compaction in candidate order: folded pairs, freed slots, kept leaving keys ----
+        {
             const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-            if (nU > C && C == 0) {
-                for (int u = lane; u < nU; u += 64) keep[u] = 0;
-            } else if (nU > C) {
-                uint32_t lo = 0xffffffffu, hi = 0u;
-#pragma unroll 4
-                for (int u = lane; u < nU; u += 64) { lo = min(lo, ebits[u]); hi = max(hi, ebits[u]); }
-                const uint32_t minb = wave_min_u32(lo);
-                // monotone bin of an SRE bit pattern (same formula in both passes)
-                const float bscale = (float)NB / ((float)(wave_max_u32(hi) - minb) + 1.0f);
-                auto bin_of = [&](uint32_t x) { return min(NB - 1, (int)((float)(x - minb) * bscale)); };
-#pragma unroll
-                for (int k = 0; k < NB / 64; ++k) hist[lane * (NB / 64) + k] = 0;
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll 4
-                for (int u = lane; u < nU; u += 64) atomicAdd(&hist[bin_of(ebits[u])], 1);
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                // lane l holds bins NB-1-4l .. NB-4-4l (highest first)
-                int cb[4], tot = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) { cb[k] = hist[NB - 1 - (4 * lane + k)]; tot += cb[k]; }
-                int incl = tot;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int up = __shfl_up(incl, o, 64);
-                    if (lane >= o) incl += up;
-                }
-                const int excl = incl - tot;
-                int bsel = -1, above = 0;
-                if (excl < C && incl >= C) {
-                    int cum = excl;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if (bsel < 0 && cum + cb[k] >= C) { bsel = NB - 1 - (4 * lane + k); above = cum; }
-                        cum += cb[k];
-                    }
-                }
-                const uint64_t hit = __ballot(bsel >= 0);
-                const int src = __ffsll((long long)hit) - 1;
-                const int bstar = __shfl(bsel, src, 64);
-                const int need = C - __shfl(above, src, 64);
-                int m = 0;
-#pragma unroll 4
-                for (int base = 0; base < nU; base += 64) {
-                    const int u = base + lane;
-                    const int bin = u < nU ? bin_of(ebits[u]) : -1;
-                    if (u < nU && bin != bstar) keep[u] = bin > bstar;
-                    const bool mb = u < nU && bin == bstar;
-                    const uint64_t bm = __ballot(mb);
-                    if (mb) memb[m + __popcll(bm & lt)] = u;
-                    m += __popcll(bm);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                for (int i = lane; i < m; i += 64) {
-                    const int u = memb[i];
-                    const uint32_t eu = ebits[u];
-                    const int pu = cand_pos(u);
-                    int rank = 0;
-                    for (int j2 = 0; j2 < m; ++j2) {
-                        const int v2 = memb[j2];
-                        const uint32_t ev = ebits[v2];
-                        rank += (ev > eu) || (ev == eu && cand_pos(v2) < pu);
-                    }
-                    keep[u] = rank < need;
-                }
-            } else {
-                for (int u = lane; u < nU; u += 64) keep[u] = 1;
+            const int nblk = (nU + 63) / 64;
+            for (int j = wave; j < nblk; j += NW) {
+                const int u = j * 64 + lane;
+                const bool valid = u < nU;
+                const bool kp = valid && keep[u];
+                const int cF = __popcll(__ballot(valid && !kp));
+                const int cFr = __popcll(__ballot(valid && u < cnt && !kp));
+                const int cK = __popcll(__ballot(valid && u >= cnt && kp));
+                if (lane == 0) { bcnt[4 * j] = cF; bcnt[4 * j + 1] = cFr; bcnt[4 * j + 2] = cK; }
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            int nF = 0, nFr = 0, nK = 0;
-#pragma unroll 4
-            for (int base = 0; base < nU; base += 64) {
-                const int u = base + lane;
+            __syncthreads();
+            for (int j = wave; j < nblk; j += NW) {
+                int oF = 0, oFr = 0, oK = 0;
+                for (int j2 = 0; j2 < j; ++j2) { oF += bcnt[4 * j2]; oFr += bcnt[4 * j2 + 1]; oK += bcnt[4 * j2 + 2]; }
+                const int u = j * 64 + lane;
                 const bool valid = u < nU;
                 const bool kp = valid && keep[u];
                 const bool isF = valid && !kp;
                 const bool isFr = valid && u < cnt && !kp;
                 const bool isK = valid && u >= cnt && kp;
                 const uint64_t bF = __ballot(isF), bFr = __ballot(isFr), bK = __ballot(isK);
-                if (isF) fold[nF + __popcll(bF & lt)] = u;
-                if (isFr) freed[nFr + __popcll(bFr & lt)] = u;
-                if (isK) keptE[nK + __popcll(bK & lt)] = u;
-                nF += __popcll(bF);
-                nFr += __popcll(bFr);
-                nK += __popcll(bK);
+                if (isF) fold[oF + __popcll(bF & lt)] = u;
+                if (isFr) freed[oFr + __popcll(bFr & lt)] = u;
+                if (isK) keptE[oK + __popcll(bK & lt)] = u;
+                if (j == nblk - 1 && lane == 0) {
+                    misc[5] = oF + __popcll(bF);
+                    misc[6] = oFr + __popcll(bFr);
+                    misc[7] = oK + __popcll(bK);
+                }
             }
-            if (lane == 0) { misc[5] = nF; misc[6] = nFr; misc[7] = nK; }
+            if (nblk == 0 && tid == 0) { misc[5] = 0; misc[6] = 0; misc[7] = 0; }
         }
         __syncthreads();
         const int nF = misc[5], nFr = misc[6], nK = misc[7];
