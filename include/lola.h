@@ -141,8 +141,13 @@ lola_status lola_read_cache(const lola_config* cfg, const void* state, int32_t b
                             int64_t* tokens_seen, void* stream);
 
 /* SYNCHRONOUS: waits for `stream`, then reads the state header and returns
- * LOLA_OK if it was written by lola_init_state for this config and batch,
- * LOLA_ERR_BAD_STATE otherwise. */
+ * LOLA_OK if it was written by lola_init_state for this config and batch and
+ * no call has marked it faulted, LOLA_ERR_BAD_STATE otherwise.  With bf16 io
+ * and few enough (sequence, KV head) chains to be resident together, the
+ * interval scan of lola_prefill_chunk spreads each chain over head_dim/16
+ * workgroups (a cooperative launch) that wait for one another once per
+ * interval; a wait that does not end within a fixed bound marks the state
+ * faulted instead of hanging. */
 lola_status lola_check_state(const lola_config* cfg, const void* state, int32_t batch, void* stream);
 
 /* Static text for a status code (never NULL). */

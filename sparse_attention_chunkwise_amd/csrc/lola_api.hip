@@ -1,5 +1,6 @@
 // C ABI of liblola: argument checks, layouts and kernel launches.
 // Every check happens on the host before anything is enqueued.
+#include <stdlib.h>
 #include <string.h>
 
 #include "lola_decode.h"
@@ -8,6 +9,7 @@
 #include "lola_output.h"
 #include "lola_decode_bf16.h"
 #include "lola_prefill.h"
+#include "lola_scan_split.h"
 
 using namespace lola;
 
@@ -82,6 +84,30 @@ hipError_t mark(void* const* events, int i, hipStream_t s)
     return hipEventRecord((hipEvent_t)events[i], s);
 }
 
+// The split scan needs every block of a chain resident at once: a cooperative
+// launch on a device that supports it, with the grid within the device's
+// co-resident capacity.  LOLA_SCAN_SPLIT=0 in the environment selects the
+// one-block-per-chain scan everywhere.
+bool split_allowed()
+{
+    const char* e = getenv("LOLA_SCAN_SPLIT");
+    return !(e && e[0] == '0');
+}
+
+template <typename K>
+bool split_fits(K kernel, int blocks, size_t lds)
+{
+    int dev = 0, coop = 0, ncu = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (allow_lds(kernel, lds) != hipSuccess) return false;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(kernel), kSplitThreads,
+                                                     lds) != hipSuccess)
+        return false;
+    return (int64_t)per * ncu >= blocks;
+}
+
 template <int D, int F, typename T>
 lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
 {
@@ -91,9 +117,24 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     dim3 gp((a.wl.X + d.C + 63) / 64, chains);
     hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
-    const size_t scan_lds = scan_smem(D, F, d.C, d.L, sizeof(T)).total;
-    if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
-    hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(scan_threads(D)), scan_lds, s, a);
+    bool split = false;
+    if constexpr (sizeof(T) == 2) {
+        const size_t lds = split_smem(F, d.C, d.L).total;
+        if (split_allowed() && split_fits(scan_split_kernel<D, F>, split_blocks(D, chains), lds)) {
+            if (allow_lds(scan_split_kernel<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
+            void* params[] = {&a};
+            if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(scan_split_kernel<D, F>),
+                                           dim3(split_blocks(D, chains)), dim3(kSplitThreads), params,
+                                           (unsigned)lds, s) != hipSuccess)
+                return LOLA_ERR_HIP;
+            split = true;
+        }
+    }
+    if (!split) {
+        const size_t scan_lds = scan_smem(D, F, d.C, d.L, sizeof(T)).total;
+        if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
+        hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(scan_threads(D)), scan_lds, s, a);
+    }
     if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
     if constexpr (sizeof(T) == 2) {
         const int wpi = (d.G * d.L + kOutRows - 1) / kOutRows;
@@ -272,7 +313,8 @@ lola_status lola_check_state(const lola_config* cfg, const void* state, int32_t 
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_ERR_HIP;
     StateHeader h;
     if (hipMemcpy(&h, state, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return LOLA_ERR_HIP;
-    if (h.magic != kMagic || h.version != kVersion || h.cfg_hash != cfg_hash(cfg, batch) || h.batch != batch)
+    if (h.magic != kMagic || h.version != kVersion || h.cfg_hash != cfg_hash(cfg, batch) || h.batch != batch ||
+        h.fault != 0)
         return LOLA_ERR_BAD_STATE;
     return LOLA_OK;
 }

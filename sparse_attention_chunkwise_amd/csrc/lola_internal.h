@@ -35,7 +35,8 @@ struct StateHeader {
     uint32_t version;
     uint64_t cfg_hash;
     int32_t batch;
-    int32_t pad[3];
+    int32_t fault;  // nonzero once a prefill scan gave up waiting for a sibling workgroup
+    int32_t pad[2];
 };
 
 // State buffer: header | W [Hkv][Fh][D] f32 | Wb [Hkv][3][Fh][D] bf16 (three parts of W, largest first) | chains [B][Hkv]
@@ -82,9 +83,12 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 //   phi, features in the SRE operand order) |
 //   snapH [B][Hkv][NI][D][F] H^T: f32 for f32 io; bf16 in operand order for bf16 io |
 //   snapS [B][Hkv][NI][F] f32 |
-//   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32
+//   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32 |
+//   xsync [B][Hkv][16] u32 (give-up flag, reads-done counter) |
+//   xe [B][Hkv][2][D/16][C + L] u64 (per-column-slice partial SRE: exchange
+//      number << 32 | f32 bits; two buffers used alternately)
 struct WsLayout {
-    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, snapH, snapS, snapRef, snapN;
+    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, snapH, snapS, snapRef, snapN, xsync, xe;
     size_t total;
     int X, NI;
 };
@@ -110,6 +114,8 @@ inline __host__ __device__ WsLayout ws_layout(const Dims& d, int B, int n)
     s.snapS = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F, 256);
     s.snapRef = off;  off = align_up(off + sizeof(int32_t) * ch * s.NI * Cp, 256);
     s.snapN = off;    off = align_up(off + sizeof(int32_t) * ch * s.NI, 256);
+    s.xsync = off;    off = align_up(off + sizeof(uint32_t) * 16 * ch, 256);
+    s.xe = off;       off = align_up(off + sizeof(uint64_t) * ch * 2 * (d.D / 16) * (size_t)(d.C + d.L), 256);
     s.total = off;
     return s;
 }

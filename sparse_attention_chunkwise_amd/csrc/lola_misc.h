@@ -16,6 +16,7 @@ __global__ __launch_bounds__(256) void init_kernel(Args a, const float* W, uint6
             h->version = kVersion;
             h->cfg_hash = cfg_hash;
             h->batch = a.B;
+            h->fault = 0;
         }
         float* Wd = (float*)(a.state + a.sl.W);
         const size_t nw = (size_t)a.d.Hkv * a.d.Fh * a.d.D;

@@ -130,6 +130,13 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
     const float* W = (const float*)(a.state + a.sl.W) + (size_t)g * Fh * D;
     for (int i = threadIdx.x; i < Fh * D; i += 256) Ws[i / D][i % D] = W[i];
     if (blockIdx.x == 0 && threadIdx.x == 0 && g == 0) ((int64_t*)(a.ws + a.wl.t0))[b] = t0;
+    if (blockIdx.x == 0 && threadIdx.x < 16) ((uint32_t*)(a.ws + a.wl.xsync))[chain * 16 + threadIdx.x] = 0u;
+    {
+        // exchange slots of the split scan start empty (exchange number 0)
+        const size_t nx = (size_t)2 * (D / 16) * (C + a.d.L);
+        uint64_t* xe = (uint64_t*)(a.ws + a.wl.xe) + (size_t)chain * nx;
+        for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nx; i += (size_t)gridDim.x * 256) xe[i] = 0ull;
+    }
 
     for (int rr = 0; rr < RPW; ++rr) {
         const int row = (blockIdx.x * 4 + wave) * RPW + rr;

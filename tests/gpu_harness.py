@@ -121,6 +121,10 @@ class Stepper:
                 self.forced_count += int(fc)
         return gout, ref
 
+    def healthy(self) -> bool:
+        """The state header is intact and no scan gave up waiting (synchronises)."""
+        return lola.check_state(self.layer, self.state, self.B) == 0
+
     def compare_state(self, chain_mask=None):
         """H, s relative errors (max over chains) and exact cache key/value equality."""
         L = self.layer

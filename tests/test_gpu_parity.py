@@ -26,6 +26,7 @@ def _stepped(layer, B, W, Q, K, V, state_every=8, label=""):
         if state_every and (ci % state_every == state_every - 1 or e == T):
             eh, es = st.compare_state()
             assert eh <= tol and es <= tol, f"{label} interval {ci}: H {eh:.3g} s {es:.3g}"
+    assert st.healthy(), f"{label}: state marked faulted"
     print(f"{label}: worst output rel err {worst:.3g}, near ties adopted {st.forced_count}", flush=True)
     return st
 
@@ -41,6 +42,7 @@ def _full(layer, B, W, Q, K, V, calls=None):
                                  dev(V[:, a:a + n], layer)))
         a += n
     out = torch.cat(outs, dim=1)
+    assert lola.check_state(layer, state, B) == 0, "state marked faulted"
     return out, lola.read_cache(layer, state, B), state
 
 
@@ -110,6 +112,16 @@ EDGE = [
     ("bf16_d64", I.LayerConfig(4, 4, 64, 32, 8, 12, 16, "bf16"), 1, 130),
     ("max_interval", I.LayerConfig(2, 1, 64, 32, 16, 40, 256, "f32"), 1, 600),
     ("max_cache", I.LayerConfig(2, 1, 64, 32, 8, 1024, 128, "bf16"), 1, 1500),
+    # bf16 io runs the scan with each chain spread over head_dim/16 workgroups
+    ("bf16_no_window", I.LayerConfig(2, 2, 64, 32, 0, 6, 8, "bf16"), 1, 61),
+    ("bf16_no_cache", I.LayerConfig(2, 1, 64, 32, 4, 0, 8, "bf16"), 1, 40),
+    ("bf16_interval_1", I.LayerConfig(2, 1, 64, 32, 4, 5, 1, "bf16"), 1, 37),
+    ("bf16_cache_beyond_seq", I.LayerConfig(2, 1, 64, 32, 4, 128, 8, "bf16"), 1, 90),
+    ("bf16_interval_longer_than_window", I.LayerConfig(4, 1, 128, 64, 5, 7, 24, "bf16"), 2, 101),
+    ("bf16_d128_f64", I.LayerConfig(2, 2, 128, 32, 6, 9, 10, "bf16"), 1, 55),
+    ("bf16_d64_f128", I.LayerConfig(2, 1, 64, 64, 6, 9, 10, "bf16"), 1, 55),
+    ("bf16_twelve_chains", I.LayerConfig(4, 4, 64, 32, 8, 12, 16, "bf16"), 3, 90),
+    ("bf16_max_interval", I.LayerConfig(2, 1, 64, 32, 16, 40, 256, "bf16"), 1, 600),
 ]
 
 
@@ -117,6 +129,17 @@ EDGE = [
 def test_edge_stepped(name, layer, B, T):
     W, Q, K, V = I.random_case(100 + len(name), layer, B, T)
     _stepped(layer, B, W, Q, K, V, state_every=4, label=name)
+
+
+ONE_BLOCK = [e for e in EDGE if e[0] in ("bf16_ragged", "bf16_d64", "bf16_max_interval", "bf16_no_cache")]
+
+
+@pytest.mark.parametrize("name,layer,B,T", ONE_BLOCK, ids=[e[0] for e in ONE_BLOCK])
+def test_edge_stepped_one_block_scan(name, layer, B, T, monkeypatch):
+    """bf16 io with the scan forced to one workgroup per chain (the path large batches take)."""
+    monkeypatch.setenv("LOLA_SCAN_SPLIT", "0")
+    W, Q, K, V = I.random_case(100 + len(name), layer, B, T)
+    _stepped(layer, B, W, Q, K, V, state_every=4, label=name + "/one-block")
 
 
 @pytest.mark.parametrize("name,layer,B,T", EDGE, ids=[e[0] for e in EDGE])
