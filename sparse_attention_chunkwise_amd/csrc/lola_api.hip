@@ -120,11 +120,19 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     bool split = false;
     if constexpr (sizeof(T) == 2) {
         const size_t lds = split_smem(F, d.C, d.L).total;
-        if (split_allowed() && split_fits(scan_split_kernel<D, F>, split_blocks(D, chains), lds)) {
+        // as many candidate groups per column slice (4, 2, then 1) as the device holds at once
+        int pu = 0;
+        if (split_allowed())
+            for (int g : {4, 2, 1})
+                if (split_fits(scan_split_kernel<D, F>, split_blocks(D, chains, g), lds)) {
+                    pu = g;
+                    break;
+                }
+        if (pu > 0) {
             if (allow_lds(scan_split_kernel<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
             void* params[] = {&a};
             if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(scan_split_kernel<D, F>),
-                                           dim3(split_blocks(D, chains)), dim3(kSplitThreads), params,
+                                           dim3(split_blocks(D, chains, pu)), dim3(kSplitThreads), params,
                                            (unsigned)lds, s) != hipSuccess)
                 return LOLA_ERR_HIP;
             split = true;
