@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     int* misc = (int*)(smem + sm.misc);
 
     const int b = chain / d.Hkv, g = chain % d.Hkv;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave branches scalar
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ws_t0(a, b);
@@ -423,21 +424,23 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     // Threshold bit by bit (SRE >= 0: bit 31 is clear): the largest t with
                     // #{key >= t} >= C.  Slots past nU hold 0 and never count for t > 0.
                     // Stop early once exactly C keys reach the threshold.
+                    // (tau, t and the counts are wave-uniform; readfirstlane keeps them scalar)
                     uint32_t tau = 0u;
-                    bool exact = false;
-                    for (int bit = 30; bit >= 0; --bit) {
-                        const uint32_t t = tau | (1u << bit);
-                        int ge = 0;
+                    int bit = 30, ge = 0;
+                    do {
+                        const uint32_t t = __builtin_amdgcn_readfirstlane(tau | (1u << bit));
+                        uint64_t bal[NC];  // all compares first, then the counts
 #pragma unroll
-                        for (int i = 0; i < NC; ++i) ge += __popcll(__ballot(key[i] >= t));
-                        if (ge >= C) {
-                            tau = t;
-                            if (ge == C) {
-                                exact = true;
-                                break;
-                            }
-                        }
-                    }
+                        for (int i = 0; i < NC; ++i) bal[i] = __ballot(key[i] >= t);
+                        ge = 0;
+#pragma unroll
+                        for (int i = 0; i < NC; ++i) ge += __popcll(bal[i]);
+                        ge = __builtin_amdgcn_readfirstlane(ge);
+                        tau = ge >= C ? t : tau;
+                        bit = __builtin_amdgcn_readfirstlane(bit - 1);
+                    } while (bit >= 0 && ge != C);
+                    const bool exact = ge == C;
+                    tau = __builtin_amdgcn_readfirstlane(tau);
                     int above = 0, ties = 0;
                     if (!exact) {
 #pragma unroll
