@@ -103,6 +103,7 @@ class Stepper:
         else:
             out = lola.prefill(L, self.state, dev(q, L), dev(k, L), dev(v, L))
             gout = host(out)
+        self.last_out = out  # device tensor of this step's outputs
         sets = self.gpu_cache_sets()
         C = L.cache_cap
         forced = np.full((self.B, L.n_kv_heads, 1, max(C, 1)), -1, np.int64)
