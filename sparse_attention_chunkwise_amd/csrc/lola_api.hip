@@ -115,7 +115,10 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     const int chains = a.B * d.Hkv;
     if (mark(ev, 0, s) != hipSuccess) return LOLA_ERR_HIP;
     dim3 gp((a.wl.X + d.C + 63) / 64, chains);
-    hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((prologue_bf16_kernel<D, F / 2>), gp, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
     bool split = false;
     if constexpr (sizeof(T) == 2) {

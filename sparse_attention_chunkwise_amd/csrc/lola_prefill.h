@@ -211,6 +211,134 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
     }
 }
 
+// Prologue for bf16 io: same rows and layouts, computed 16 rows per wave with
+// MFMA.  z^T = W x^T uses W in three bf16 parts (the products with the bf16 key
+// are exact, sums in fp32); lane (r16, qg) then holds features ft*16 + 4qg + i of
+// row r16 and the two softmaxes combine the four lanes of a row by shuffles.
+// grid (ceil((X + C) / 64), B*Hkv), block 256.
+template <int D, int Fh>
+__global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a)
+{
+    constexpr int F = 2 * Fh, FTH = Fh / 16, DS = D / 32;
+    const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    const int w = a.d.w, C = a.d.C, X = a.wl.X, Cp = C > 0 ? C : 1;
+    Chain ch = chain_of(a, chain);
+    const int64_t t0 = ch.tok();
+    const int cnt0 = min(max(ch.cnt(), 0), C);
+    if (blockIdx.x == 0 && tid == 0 && g == 0) ((int64_t*)(a.ws + a.wl.t0))[b] = t0;
+    if (blockIdx.x == 0 && tid < 16) ((uint32_t*)(a.ws + a.wl.xsync))[chain * 16 + tid] = 0u;
+    {
+        // exchange slots of the split scan start empty (exchange number 0)
+        const size_t nx = (size_t)2 * (D / 16) * (C + a.d.L);
+        uint64_t* xe = (uint64_t*)(a.ws + a.wl.xe) + (size_t)chain * nx;
+        for (size_t i = (size_t)blockIdx.x * 256 + tid; i < nx; i += (size_t)gridDim.x * 256) xe[i] = 0ull;
+    }
+    // source key row of an extended-sequence or cache row (nullptr: none, phi = 0)
+    auto row_src = [&](int row, bool v) -> const bf16* {
+        if (row < w) {
+            const int64_t p = t0 - w + row;
+            if (p < 0) return nullptr;
+            return (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)(p % w) * D;
+        }
+        if (row < X) return (const bf16*)(v ? a.v : a.k) + (((size_t)b * a.n + (row - w)) * a.d.Hkv + g) * D;
+        if (row < X + C && row - X < cnt0) return (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (size_t)(row - X) * D;
+        return nullptr;
+    };
+    // raw copies of the window ring and the cache as they stand at the call start
+    for (int idx = tid; idx < 64 * (D / 8); idx += 256) {
+        const int row = blockIdx.x * 64 + idx / (D / 8), u8 = (idx % (D / 8)) * 8;
+        bf16* dk = nullptr;
+        bf16* dv = nullptr;
+        if (row < w) {
+            dk = (bf16*)(a.ws + a.wl.ring0_k) + ((size_t)chain * w + row) * D;
+            dv = (bf16*)(a.ws + a.wl.ring0_v) + ((size_t)chain * w + row) * D;
+        } else if (row >= X && row < X + C) {
+            dk = (bf16*)(a.ws + a.wl.cache0_k) + ((size_t)chain * Cp + (row - X)) * D;
+            dv = (bf16*)(a.ws + a.wl.cache0_v) + ((size_t)chain * Cp + (row - X)) * D;
+        }
+        if (!dk) continue;
+        const bf16* sk = row_src(row, false);
+        const bf16* sv = row_src(row, true);
+        *(uint4*)(dk + u8) = sk ? *(const uint4*)(sk + u8) : make_uint4(0, 0, 0, 0);
+        *(uint4*)(dv + u8) = sv ? *(const uint4*)(sv + u8) : make_uint4(0, 0, 0, 0);
+    }
+    // phi rows: this wave's 16 rows, row r16 of the tile is MFMA column r16
+    const int row = blockIdx.x * 64 + wave * 16 + r16;
+    const bf16* src = row < X + C ? row_src(row, false) : nullptr;
+    bf16x8 xb[DS];
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks)
+        xb[ks] = __builtin_bit_cast(bf16x8, src ? *(const uint4*)(src + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0));
+    const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
+    floatx4 zt[FTH];
+#pragma unroll
+    for (int ft = 0; ft < FTH; ++ft) {
+        zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks)
+#pragma unroll
+            for (int part = 0; part < 3; ++part)
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    *(const bf16x8*)(Wb + (size_t)part * Fh * D + (ft * 16 + r16) * D + ks * 32 + qg * 8), xb[ks], zt[ft],
+                    0, 0, 0);
+    }
+    float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+    for (int ft = 0; ft < FTH; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            zmax = fmaxf(zmax, zt[ft][i]);
+            zmin = fminf(zmin, zt[ft][i]);
+        }
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+    zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+    zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+    float ep[FTH][4], en[FTH][4], sp = 0.f, sn = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < FTH; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ep[ft][i] = expf(zt[ft][i] - zmax);
+            en[ft][i] = expf(zmin - zt[ft][i]);
+            sp += ep[ft][i];
+            sn += en[ft][i];
+        }
+    sp += __shfl_xor(sp, 16, 64);
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 16, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    if (row >= X + C) return;
+    const bool valid = src != nullptr;
+    float ph[2 * FTH][4];  // feature tile T: + half T < FTH, - half T >= FTH
+#pragma unroll
+    for (int ft = 0; ft < FTH; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ph[ft][i] = valid ? ep[ft][i] / sp : 0.f;
+            ph[FTH + ft][i] = valid ? en[ft][i] / sn : 0.f;
+        }
+    float* po = row < X ? ws_phiX(a, chain, row) : ws_cphi(a, chain, row - X);
+    uint16_t* ps = row < X ? ws_phiS(a, chain, row) : ws_cphiS(a, chain, row - X);
+#pragma unroll
+    for (int T = 0; T < 2 * FTH; ++T)
+        *(float4*)(po + T * 16 + qg * 4) = make_float4(ph[T][0], ph[T][1], ph[T][2], ph[T][3]);
+    // hi / lo parts in operand order: tiles 2m and 2m+1 fill positions m*32 + qg*8 + 0..7
+#pragma unroll
+    for (int m = 0; m < FTH; ++m) {
+        u16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = ph[2 * m + (j >> 2)][j & 3];
+            hi[j] = from_f32<bf16>(x).x;
+            lo[j] = from_f32<bf16>(x - __uint_as_float((uint32_t)hi[j] << 16)).x;
+        }
+        *(u16x8*)(ps + m * 32 + qg * 8) = hi;
+        *(u16x8*)(ps + F + m * 32 + qg * 8) = lo;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 2. scan: one workgroup per chain (D/16 waves), intervals in order.
 //
