@@ -1,7 +1,7 @@
 // Output pass for bf16 io (gfx950), LDS-staged.
 //
-// One workgroup (4 waves) handles 128 query rows of one (interval, chain);
-// each wave owns 32 rows as two 16-column MFMA tiles (the queries are the
+// One workgroup (8 waves) handles 128 query rows of one (interval, chain);
+// each wave owns 16 rows as one 16-column MFMA tile (the queries are the
 // columns, so softmax statistics live in the lanes).  Per workgroup:
 //   - H_c^T (bf16, features in operand order) and W (bf16 hi + lo) staged once;
 //   - z^T = W Q^T gives phi(q) (two softmax halves over the features),
@@ -23,6 +23,7 @@ namespace lola {
 
 constexpr int kOutRows = 128;  // query rows per workgroup
 constexpr int kKeyBlock = 32;
+constexpr int kOutThreads = 512;  // 8 waves x 16 query rows
 
 struct OutSmem {
     size_t sP, refs, Ks, VT, Pk, total;
@@ -45,9 +46,10 @@ __host__ __device__ inline OutSmem out_smem(int D, int F, int C)
 __device__ __forceinline__ int key_perm(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
 
 template <int D, int F>
-__global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Args a)
+__global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 {
-    constexpr int NW = 4, RT = 2, KB = kKeyBlock, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
+    constexpr int NT = kOutThreads, NW = NT / 64, RT = 1, KB = kKeyBlock, Fh = F / 2, FM = F / 32, DS = D / 32,
+                  DT = D / 16;
     constexpr int KP = D + 8, VP = KB + 8, PP = F + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
@@ -76,11 +78,11 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
     const uint16_t* Wlg = Whg + (size_t)Fh * D;
     {
         const float* sS = (const float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
-        for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = sS[i];
+        for (int i = tid; i < F; i += NT) sP[perm_pos(i)] = sS[i];
         const int Cp0 = d.C > 0 ? d.C : 1;
         const int cc0 = ((const int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c];
         const int* sr0 = (const int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp0;
-        for (int i = tid; i < cc0; i += 256) srefL[i] = sr0[i];
+        for (int i = tid; i < cc0; i += NT) srefL[i] = sr0[i];
     }
 
     // ---- this lane's queries (columns r16 of the wave's two row tiles) ----
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
     bf16x8 qf[RT][DS];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int r = rblk * kOutRows + wave * 32 + rt * 16 + r16;
+        const int r = rblk * kOutRows + wave * (16 * RT) + rt * 16 + r16;
         const int hl = r / L, ti = r % L;
         qv[rt] = r < rows && ti < Lc;
         hq_[rt] = g * G + (qv[rt] ? hl : 0);
@@ -197,15 +199,15 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
     const int xs0 = (int)(sp0 - (t0 - w));
     const float tau = d.tau;
     const int64_t lastPend = ep - 1 - w;
-    constexpr int KU = KB * D / 8 / 256;   // 16-byte units per thread for K (and V)
-    constexpr int PU = KB * F / 8 / 256;   // for phi(K)
-    constexpr int VPU = (KB / 2) * (D / 8);  // (key pair, 8-value unit) items for V
-    static_assert(VPU <= 256, "one V key-pair unit per thread at most");
+    constexpr int KU = (KB * D / 8 + NT - 1) / NT;  // 16-byte units per thread for K
+    constexpr int PU = (KB * F / 8 + NT - 1) / NT;  // for phi(K)
+    constexpr int VPU = (KB / 2) * (D / 8);         // (key pair, 8-value unit) items for V
+    static_assert(VPU <= NT, "one V key-pair unit per thread at most");
     uint4 pk[KU], pv[2], pp[PU];
 #define LOLA_OUT_PREFETCH(BASE)                                                                                      \
     do {                                                                                                             \
         _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
-            const int idx = tid + k * 256, kr = idx / (D / 8), un = idx % (D / 8);                                   \
+            const int idx = tid + k * NT, kr = (idx / (D / 8)) % KB, un = idx % (D / 8);                             \
             const int kidx = (BASE) + kr, kc = kidx < nK ? kidx : 0;                                                 \
             const bf16* kp = kc < nSpan ? xrow_k<bf16>(a, chain, b, g, xs0 + kc) : ref_k<bf16>(a, chain, b, g, sref[kc - nSpan]); \
             const uint4 k4 = *(const uint4*)(kp + un * 8);                                                           \
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
             }                                                                                                        \
         }                                                                                                            \
         _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
-            const int idx = tid + k * 256, kr = idx / (F / 8), un = idx % (F / 8), kidx = (BASE) + kr;               \
+            const int idx = tid + k * NT, kr = (idx / (F / 8)) % KB, un = idx % (F / 8), kidx = (BASE) + kr;         \
             const bool want = kidx < nSpan && sp0 + kidx <= lastPend;                                                \
             const uint4 p4 = *(const uint4*)(ws_phiS(a, chain, xs0 + (want ? kidx : 0)) + un * 8);                   \
             pp[k] = want ? p4 : make_uint4(0, 0, 0, 0);                                                              \
@@ -232,8 +234,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
         __syncthreads();  // the previous block (or W) is no longer read
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
-            const int idx = tid + k * 256, kr = idx / (D / 8), un = idx % (D / 8);
-            *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
+            const int idx = tid + k * NT, kr = idx / (D / 8), un = idx % (D / 8);
+            if (idx < KB * D / 8) *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
         }
         if (tid < VPU) {
             // keys 2pr, 2pr+1 sit next to each other in the operand order
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void output_kernel_bf16(Ar
         }
 #pragma unroll
         for (int k = 0; k < PU; ++k) {
-            const int idx = tid + k * 256, kr = idx / (F / 8), un = idx % (F / 8);
-            *(uint4*)(Pk + kr * PP + un * 8) = pp[k];
+            const int idx = tid + k * NT, kr = idx / (F / 8), un = idx % (F / 8);
+            if (idx < KB * F / 8) *(uint4*)(Pk + kr * PP + un * 8) = pp[k];
         }
         __syncthreads();
         if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB);
