@@ -31,6 +31,7 @@
 // within a fixed number of polls marks the state as faulted and returns.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "lola_prefill.h"
@@ -43,7 +44,7 @@ constexpr int kSelChunks = (kMaxCand + 63) / 64;      // 64-candidate chunks a w
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 struct SplitSmem {
-    size_t PR, VS, AX, s, sparts, ebits, foldu, ucode, cref, cpos, freed, tiep, misc, total;
+    size_t PR, VS, AX, s, sparts, ebits, foldc, ucode, cref, cpos, freed, tiep, misc, total;
 };
 
 __host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
@@ -57,7 +58,7 @@ __host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
     m.s = off;      off += align_up(sizeof(float) * F, 16);
     m.sparts = off; off += align_up(sizeof(uint16_t) * 3 * (size_t)F, 16);            // [3][F]
     m.ebits = off;  off += sizeof(uint32_t) * U;
-    m.foldu = off;  off += sizeof(int) * U;
+    m.foldc = off;  off += sizeof(int) * U;
     m.ucode = off;  off += sizeof(int) * 2 * U;
     m.cref = off;   off += sizeof(int) * Cp;
     m.cpos = off;   off += sizeof(int) * Cp;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     float* sP = (float*)(smem + sm.s);             // s, operand order
     uint16_t* sParts = (uint16_t*)(smem + sm.sparts);
     uint32_t* ebits = (uint32_t*)(smem + sm.ebits);
-    int* foldu = (int*)(smem + sm.foldu);          // fold index -> candidate
+    int* foldc = (int*)(smem + sm.foldc);          // fold index -> candidate code
     int* ucodeb = (int*)(smem + sm.ucode);         // two candidate lists (this interval, next)
     int* cref = (int*)(smem + sm.cref);
     int* cpos = (int*)(smem + sm.cpos);
@@ -226,13 +227,13 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     };
 
     // Partial SRE of this block's candidate tiles t = ju + PU * i, i = ibase + wave +
-    // NW * k (k < G): G tiles per wave are loaded, then computed two at a time.
-    auto sre_group = [&](auto gTag, const int* uc, int nUq, int ibase, uint64_t* xw, uint32_t tag,
-                         const bf16x8* Ah, const bf16x8* Al, const bf16x8* As) {
+    // NW * k (k < G): sre_load fetches the phi rows (hi, lo) and the values of a
+    // wave's G tiles, sre_math computes them two at a time and publishes the
+    // partial errors.
+    auto sre_load = [&](auto gTag, const int* uc, int nUq, int ibase, uint4 (&fh)[decltype(gTag)::value][FM],
+                        uint4 (&fl)[decltype(gTag)::value][FM], uint2 (&fv)[decltype(gTag)::value]) {
         constexpr int G = decltype(gTag)::value;
         const int T = (nUq + 15) / 16;
-        uint4 fh[G][FM], fl[G][FM];
-        uint2 fv[G];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             int t = ju + PU * (ibase + wave + k * NW);
@@ -248,6 +249,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             }
             fv[k] = *(const uint2*)(code_v(code) + col0 + qg * 4);
         }
+    };
+    auto sre_math = [&](auto gTag, int nUq, int ibase, uint64_t* xw, uint32_t tag, const bf16x8* Ah,
+                        const bf16x8* Al, const bf16x8* As, const uint4 (&fh)[decltype(gTag)::value][FM],
+                        const uint4 (&fl)[decltype(gTag)::value][FM], const uint2 (&fv)[decltype(gTag)::value]) {
+        constexpr int G = decltype(gTag)::value;
+        const int T = (nUq + 15) / 16;
         // two tiles at a time, m outer: consecutive MFMAs are independent
 #pragma unroll
         for (int k0 = 0; k0 < G; k0 += 2) {
@@ -295,11 +302,48 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 
     uint32_t arrivals = 0;  // exchanges this block has completed
     int cur = 0;            // candidate list of this interval: ucodeb + cur * U
+    // Operands of the next SRE when each wave has at most two tiles, loaded while
+    // the previous interval folds.  A lane keeps the candidate code of the row it
+    // holds per tile (pfcode): cache slots mostly keep their pair from one interval
+    // to the next and a tile always maps to the same wave, so only rows whose code
+    // changed are loaded again.  Where the next SRE is not needed or loads its own
+    // operands, the row of candidate code 0 (extended row 0, always present) is held.
+    using Two = std::integral_constant<int, 2>;
+    uint4 pfh[2][FM], pfl[2][FM];
+    uint2 pfv[2];
+    int pfcode[2] = {INT_MIN, INT_MIN};
+    auto tiles_of_block = [&](int nUq) { const int T = (nUq + 15) / 16; return T > ju ? (T - ju + PU - 1) / PU : 0; };
+    auto prefetch_next = [&](int nUq, const int* uc) {
+        const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW;
+        const int T = (nUq + 15) / 16;
+        int code[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            int t = ju + PU * (wave + k * NW);
+            t = t < T ? t : T - 1;
+            int u = t * 16 + r16;
+            u = u < nUq ? u : nUq - 1;
+            code[k] = use ? uc[u] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            if (code[k] != pfcode[k]) {
+                const uint16_t* p = code_phs(code[k]) + qg * 8;
+#pragma unroll
+                for (int m = 0; m < FM; ++m) {
+                    pfh[k][m] = *(const uint4*)(p + m * 32);
+                    pfl[k][m] = *(const uint4*)(p + F + m * 32);
+                }
+                pfv[k] = *(const uint2*)(code_v(code[k]) + col0 + qg * 4);
+                pfcode[k] = code[k];
+            }
+    };
     {
         const Iv v0 = interval(0);
         for (int u = tid; u < cnt + v0.nE; u += NT) ucodeb[u] = u < cnt ? cref[u] : v0.xE0 + (u - cnt);
+        lds_sync();
+        prefetch_next(cnt + v0.nE, ucodeb);
     }
-    lds_sync();
 
     for (int c = 0; c < NI; ++c) {
         const Iv iv = interval(c);
@@ -309,20 +353,24 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int T = (nU + 15) / 16;
         const int* ucode = ucodeb + cur * U;
 
-        // ---- interval-start snapshot: H^T hi parts of this block's rows, s and cache refs ----
-        if (lead && wave == 0) {
-            uint16_t* dst = (uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D +
-                            (size_t)(col0 + r16) * F + qg * 8;
+        // ---- interval-start snapshot: H^T hi parts of this block's rows, s and cache
+        //      refs (written before the fold and the selection change them) ----
+        auto snapshot = [&]() {
+            if (lead && wave == 0) {
+                uint16_t* dst = (uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D +
+                                (size_t)(col0 + r16) * F + qg * 8;
 #pragma unroll
-            for (int m = 0; m < FM; ++m) *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
-        }
-        if (lead && jw == 0) {
-            float* snapS = (float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
-            int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
-            for (int i = tid; i < F; i += NT) snapS[i] = sP[perm_pos(i)];
-            for (int i = tid; i < cnt; i += NT) snapRef[i] = cref[i];
-            if (tid == 0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
-        }
+                for (int m = 0; m < FM; ++m)
+                    *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
+            }
+            if (lead && jw == 0) {
+                float* snapS = (float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
+                int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
+                for (int i = tid; i < F; i += NT) snapS[i] = sP[perm_pos(i)];
+                for (int i = tid; i < cnt; i += NT) snapRef[i] = cref[i];
+                if (tid == 0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
+            }
+        };
 
         const bool needSel = nU > C && C > 0;  // the same in every block of the chain
         if (needSel) {
@@ -336,13 +384,19 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             {
                 bf16x8 Ah[FM], Al[FM], As[FM];
                 load_A(Ah, Al, As);
-                const int TB = T > ju ? (T - ju + PU - 1) / PU : 0;  // this block's tiles
-                if (TB <= 2 * NW) sre_group(std::integral_constant<int, 2>{}, ucode, nU, 0, xw, tag, Ah, Al, As);
+                const int TB = tiles_of_block(nU);
+                if (TB <= 2 * NW)  // operands loaded during the previous fold (or before the loop)
+                    sre_math(Two{}, nU, 0, xw, tag, Ah, Al, As, pfh, pfl, pfv);
                 else
-                    for (int ib = 0; ib < TB; ib += RES)
-                        sre_group(std::integral_constant<int, GR>{}, ucode, nU, ib, xw, tag, Ah, Al, As);
+                    for (int ib = 0; ib < TB; ib += RES) {
+                        uint4 fh[GR][FM], fl[GR][FM];
+                        uint2 fv[GR];
+                        sre_load(std::integral_constant<int, GR>{}, ucode, nU, ib, fh, fl, fv);
+                        sre_math(std::integral_constant<int, GR>{}, nU, ib, xw, tag, Ah, Al, As, fh, fl, fv);
+                    }
             }
             ++arrivals;
+            snapshot();  // overlaps the wait for the other blocks' partials
 
             // ---- SRE totals: every block's partial, added in column-slice order
             //      (the same bits in every block); a slot is read again until it
@@ -398,7 +452,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             }
             lds_sync();
             if (misc[8] == (int)tag) return;  // block-uniform
-        }
+        } else
+            snapshot();
 
         // ---- wave 0: exact top-C on (SRE desc, position asc), compaction, slot
         //      updates and the next interval's candidate list ----
@@ -412,11 +467,13 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             auto select_compact = [&](auto ncTag) {
                 constexpr int NC = decltype(ncTag)::value;
                 uint32_t key[NC];
+                int ucv[NC];              // candidate codes
                 uint64_t km[NC], vm[NC];  // keep and valid masks per chunk
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
                     const int u = i * 64 + lane;
                     key[i] = (needSel && u < nU) ? ebits[u] : 0u;
+                    ucv[i] = u < nU ? ucode[u] : 0;
                     vm[i] = __ballot(u < nU);
                     km[i] = (!needSel && nU <= C) ? vm[i] : 0ull;
                 }
@@ -427,6 +484,9 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     // (tau, t and the counts are wave-uniform; readfirstlane keeps them scalar)
                     uint32_t tau = 0u;
                     int bit = 30, ge = 0;
+                    // kept as a loop: unrolled, its 31 steps would stream through the
+                    // instruction cache once per interval
+#pragma nounroll
                     do {
                         const uint32_t t = __builtin_amdgcn_readfirstlane(tau | (1u << bit));
                         uint64_t bal[NC];  // all compares first, then the counts
@@ -485,7 +545,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     const bool isF = ((vm[i] & ~km[i]) >> lane) & 1ull;
                     const bool isFr = isF && u < cnt;
                     const uint64_t bF = __ballot(isF), bFr = __ballot(isFr);
-                    if (isF) foldu[nF + __popcll(bF & lt)] = u;
+                    if (isF) foldc[nF + __popcll(bF & lt)] = ucv[i];
                     if (isFr) freed[nFr + __popcll(bFr & lt)] = u;
                     nF += __popcll(bF);
                     nFr += __popcll(bFr);
@@ -519,32 +579,51 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int nF = misc[5];
 
         // ---- fold into this block's columns: H += (phi hi + lo) v^T, s += phi hi + lo ----
-        for (int e0 = 0; e0 < nF; e0 += EC) {
-            const int ne = nF - e0 < EC ? nF - e0 : EC;
-            if (e0 > 0) lds_sync();  // the previous chunk is consumed
-            {
-                // every load of the chunk is issued before any is waited for
-                constexpr int SPT = EC * (2 * F / 8) / NT;  // 16-byte pieces per thread
-                uint4 t4[SPT];
-                uint2 t2 = make_uint2(0, 0);
-                const int ve1 = tid >> 2, vq4 = (tid & 3) * 4;  // EC * 4 == NT value pieces
+        // A chunk of up to EC folded pairs is loaded to registers (every load issued
+        // before any is waited for), stored to LDS transposed, then multiplied.
+        constexpr int SPT = EC * (2 * F / 8) / NT;  // 16-byte pieces per thread
+        const int ve1 = tid >> 2, vq4 = (tid & 3) * 4;  // EC * 4 == NT value pieces
+        uint4 t4[SPT];
+        uint2 t2;
+        // Rows past the chunk end load the chunk's last pair and are zeroed after the
+        // load, so that every lookup and load is issued without a branch.
+        auto stage_load = [&](int e0) {
+            const int ne = nF - e0 < EC ? nF - e0 : EC;  // >= 1
+            int code[SPT];
 #pragma unroll
-                for (int k = 0; k < SPT; ++k) {
-                    const int idx = tid + k * NT, e1 = idx / (2 * F / 8), c8 = (idx % (2 * F / 8)) * 8;
-                    t4[k] = e1 < ne ? *(const uint4*)(code_phs(ucode[foldu[e0 + e1]]) + c8) : make_uint4(0, 0, 0, 0);
-                }
-                if (ve1 < ne) t2 = *(const uint2*)(code_v(ucode[foldu[e0 + ve1]]) + col0 + vq4);
-#pragma unroll
-                for (int k = 0; k < SPT; ++k) {
-                    const int idx = tid + k * NT, e1 = idx / (2 * F / 8), c8 = (idx % (2 * F / 8)) * 8;
-                    *(uint4*)(PR + e1 * PRS + c8) = t4[k];
-                }
-                VS[(vq4 + 0) * EP + ve1] = (uint16_t)(t2.x & 0xffffu);
-                VS[(vq4 + 1) * EP + ve1] = (uint16_t)(t2.x >> 16);
-                VS[(vq4 + 2) * EP + ve1] = (uint16_t)(t2.y & 0xffffu);
-                VS[(vq4 + 3) * EP + ve1] = (uint16_t)(t2.y >> 16);
+            for (int k = 0; k < SPT; ++k) {
+                const int e1 = (tid + k * NT) / (2 * F / 8);
+                code[k] = foldc[e0 + (e1 < ne ? e1 : ne - 1)];
             }
-            lds_sync();
+            const int vcode = foldc[e0 + (ve1 < ne ? ve1 : ne - 1)];
+            const uint2 y = *(const uint2*)(code_v(vcode) + col0 + vq4);
+            uint4 x[SPT];
+#pragma unroll
+            for (int k = 0; k < SPT; ++k) {
+                const int c8 = ((tid + k * NT) % (2 * F / 8)) * 8;
+                x[k] = *(const uint4*)(code_phs(code[k]) + c8);
+            }
+#pragma unroll
+            for (int k = 0; k < SPT; ++k) {
+                const int e1 = (tid + k * NT) / (2 * F / 8);
+                const uint32_t keep = e1 < ne ? 0xffffffffu : 0u;
+                t4[k] = make_uint4(x[k].x & keep, x[k].y & keep, x[k].z & keep, x[k].w & keep);
+            }
+            const uint32_t vkeep = ve1 < ne ? 0xffffffffu : 0u;
+            t2 = make_uint2(y.x & vkeep, y.y & vkeep);
+        };
+        auto stage_store = [&]() {
+#pragma unroll
+            for (int k = 0; k < SPT; ++k) {
+                const int idx = tid + k * NT, e1 = idx / (2 * F / 8), c8 = (idx % (2 * F / 8)) * 8;
+                *(uint4*)(PR + e1 * PRS + c8) = t4[k];
+            }
+            VS[(vq4 + 0) * EP + ve1] = (uint16_t)(t2.x & 0xffffu);
+            VS[(vq4 + 1) * EP + ve1] = (uint16_t)(t2.x >> 16);
+            VS[(vq4 + 2) * EP + ve1] = (uint16_t)(t2.y & 0xffffu);
+            VS[(vq4 + 3) * EP + ve1] = (uint16_t)(t2.y >> 16);
+        };
+        auto fold_mma = [&]() {
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80,
                                                                  0x3f80, 0x3f80});
 #pragma unroll
@@ -573,6 +652,24 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sP[perm_pos(ft * 16 + qg * 4 + i)] += sa[i];
             }
+        };
+        if (nF > 0) {
+            stage_load(0);
+            stage_store();
+        }
+        // the next interval's SRE operands, issued once the first chunk is staged (so
+        // that they do not queue ahead of its loads); they arrive during the fold
+        prefetch_next(nUN, ucodeN);
+        if (nF > 0) {
+            lds_sync();
+            fold_mma();
+        }
+        for (int e0 = EC; e0 < nF; e0 += EC) {
+            lds_sync();  // the previous chunk is consumed
+            stage_load(e0);
+            stage_store();
+            lds_sync();
+            fold_mma();
         }
 
         // ---- new operands of H and s ----
