@@ -26,7 +26,7 @@ namespace lola {
 constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
 
 struct DecSmem {
-    size_t HhT, HlT, sP, cposL, esc, phiE, phiF, xrow, stK, stVT, misc, total;
+    size_t HhT, HlT, Wl, sP, cposL, esc, phiE, phiF, xrow, stVT, misc, total;
 };
 
 __host__ __device__ inline DecSmem dec_smem(int D, int F, int C)
@@ -36,40 +36,78 @@ __host__ __device__ inline DecSmem dec_smem(int D, int F, int C)
     size_t off = 0;
     m.HhT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
     m.HlT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
+    m.Wl = off;    off += align_up(sizeof(uint16_t) * 3 * (size_t)(F / 2) * (D + 8), 16);  // W parts, padded rows
     m.sP = off;    off += align_up(sizeof(float) * F, 16);
     m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
     m.esc = off;   off += align_up(sizeof(float) * (size_t)(C + 1), 16);
     m.phiE = off;  off += align_up(sizeof(float) * F, 16);
     m.phiF = off;  off += align_up(sizeof(float) * F, 16);
     m.xrow = off;  off += align_up(sizeof(float) * D, 16);
-    m.stK = off;   off += align_up(sizeof(uint16_t) * (size_t)kDecBlock * (D + 8), 16);
     m.stVT = off;  off += align_up(sizeof(uint16_t) * (size_t)D * (kDecBlock + 8), 16);
     m.misc = off;  off += sizeof(int) * 16;
     m.total = align_up(off, 16);
     return m;
 }
 
-// phi = [softmax(W x); softmax(-W x)] of one row by one wave in fp32 (lane i < Fh owns feature i)
-template <int D, int Fh>
-__device__ __forceinline__ void phi_row_wave(const float* W, const float* x, float* out, int lane)
+// phi = [softmax(W k); softmax(-W k)] of the 16 keys of an MFMA tile (key r16 in
+// column r16): z^T = W K^T by MFMA with W in three bf16 parts (exact products
+// against bf16 keys, fp32 sums), then one softmax per half over the features.
+// x[h] is the feature of operand slot h: slot h = 8 mf + j holds feature
+// 16 (2 mf + j / 4) + 4 qg + j % 4 (positive half for mf < F / 64).
+template <int D, int F>
+__device__ __forceinline__ void phi_tile(const uint16_t* Wl, const bf16x8* kb, int r16, int qg, float* x)
 {
-    float z = 0.f;
-    if (lane < Fh)
-        for (int j = 0; j < D; ++j) z += W[(size_t)lane * D + j] * x[j];
-    const float zmax = wave_max(lane < Fh ? z : -INFINITY);
-    const float zmin = -wave_max(lane < Fh ? -z : -INFINITY);
-    const float ep = lane < Fh ? expf(z - zmax) : 0.f;
-    const float en = lane < Fh ? expf(zmin - z) : 0.f;
-    const float sp = wave_sum(ep), sn = wave_sum(en);
-    if (lane < Fh) { out[lane] = ep / sp; out[Fh + lane] = en / sn; }
+    constexpr int Fh = F / 2, DS = D / 32, WS = D + 8;  // Wl: [3][Fh][WS] in LDS
+    floatx4 zt[Fh / 16];
+#pragma unroll
+    for (int ft = 0; ft < Fh / 16; ++ft) {
+        zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+            const int o = (ft * 16 + r16) * WS + ks * 32 + qg * 8;
+            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), kb[ks], zt[ft], 0, 0, 0);
+            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * WS + o), kb[ks], zt[ft], 0, 0, 0);
+            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + 2 * Fh * WS + o), kb[ks], zt[ft], 0, 0, 0);
+        }
+    }
+    float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+    for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+    zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+    zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+    float sp = 0.f, sn = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < Fh / 16; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e1 = expf(zt[ft][i] - zmax), e2 = expf(zmin - zt[ft][i]);
+            x[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+            x[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+            sp += e1;
+            sn += e2;
+        }
+    sp += __shfl_xor(sp, 16, 64);
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 16, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    const float isp = 1.f / sp, isn = 1.f / sn;
+#pragma unroll
+    for (int h = 0; h < F / 4; ++h) x[h] *= h < Fh / 4 ? isp : isn;
 }
+
+// feature index of operand slot h (see phi_tile) for lane group qg
+__device__ __forceinline__ int slot_feature(int h, int qg) { return (2 * (h >> 3) + ((h & 7) >> 2)) * 16 + qg * 4 + (h & 3); }
 
 template <int D, int F>
 __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
 {
     constexpr int NW = 4, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
     constexpr int KBL = kDecBlock, KW = KBL / NW;  // keys per block, per wave
-    constexpr int HP = F + 8, KP = D + 8, VP = KBL + 8;
+    constexpr int HP = F + 8, VP = KBL + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int G = d.G, w = d.w, C = d.C;
@@ -82,10 +120,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     float* phiE = (float*)(smem + sm.phiE);
     float* phiF = (float*)(smem + sm.phiF);
     float* xrow = (float*)(smem + sm.xrow);
-    uint16_t* stK = (uint16_t*)(smem + sm.stK);
+    uint16_t* Wl = (uint16_t*)(smem + sm.Wl);
     uint16_t* stVT = (uint16_t*)(smem + sm.stVT);
     int* misc = (int*)(smem + sm.misc);
-    float* mrg = (float*)(smem + sm.stK);  // merge area, reused after the key loop
+    float* mrg = (float*)(smem + sm.stVT);  // merge area, reused after the key loop
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
@@ -99,16 +137,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     const int rs = w > 0 ? (int)(t % w) : 0;
     const bf16* kE = w == 0 ? knew : ch.ring_k<bf16>() + (size_t)rs * D;
     const bf16* vE = w == 0 ? vnew : ch.ring_v<bf16>() + (size_t)rs * D;
-    const float* Wf = (const float*)(a.state + a.sl.W) + (size_t)g * Fh * D;
     const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
 
     // ---- state in: H^T hi/lo in operand order, s, cache positions ----
     {
         const float* Hst = ch.H();  // [D][F]
-        for (int i = tid; i < D * F / 4; i += 256) {
-            const int dd = (i * 4) / F, f = (i * 4) % F;
-            const float4 v4 = *(const float4*)(Hst + (size_t)dd * F + f);
-            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        constexpr int HN = D * F / 4 / 256;  // float4 per thread, all loaded before any is used
+        constexpr int WN = 3 * Fh * D / 8 / 256;  // 16-byte pieces of the W parts per thread
+        {
+            uint4 w4[WN];
+#pragma unroll
+            for (int k = 0; k < WN; ++k) w4[k] = *(const uint4*)(Wb + (size_t)(tid + k * 256) * 8);
+#pragma unroll
+            for (int k = 0; k < WN; ++k) {
+                const int e = (tid + k * 256) * 8, row = e / D, col = e % D;  // row = part * Fh + feature
+                *(uint4*)(Wl + row * (D + 8) + col) = w4[k];
+            }
+        }
+        float4 hv4[HN];
+#pragma unroll
+        for (int k = 0; k < HN; ++k) hv4[k] = *(const float4*)(Hst + (size_t)(tid + k * 256) * 4);
+#pragma unroll
+        for (int k = 0; k < HN; ++k) {
+            const int i = tid + k * 256, dd = (i * 4) / F, f = (i * 4) % F;
+            const float vv[4] = {hv4[k].x, hv4[k].y, hv4[k].z, hv4[k].w};
             uint16_t h[4], l[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -122,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = ch.s()[i];
         for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
     }
-    // query frags (columns r16 < G), phi of the leaving key (wave 3, fp32)
+    // query frags (columns r16 < G), phi of the leaving key (wave 3)
     bf16x8 qf[DS];
     {
         const bool qv = r16 < G;
@@ -133,11 +185,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             qf[ks] = __builtin_bit_cast(bf16x8, u4);
         }
     }
-    if (wave == NW - 1) {
-        for (int j = lane; j < D; j += 64) xrow[j] = hasE ? to_f32(kE[j]) : 0.f;
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        phi_row_wave<D, Fh>(Wf, xrow, phiE, lane);
+    __syncthreads();  // W parts and H in LDS
+    if (wave == NW - 1) {  // phi of the leaving key (column 0 of a tile)
+        bf16x8 kb[DS];
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+            const uint4 u4 = (r16 == 0 && hasE) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+            kb[ks] = __builtin_bit_cast(bf16x8, u4);
+        }
+        float x[F / 4];
+        phi_tile<D, F>(Wl, kb, r16, qg, x);
+        if (r16 == 0)
+#pragma unroll
+            for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[h];
     }
     __syncthreads();
 
@@ -151,9 +211,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) {
-                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + o), qf[ks], zt[ft], 0, 0, 0);
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + Fh * D + o), qf[ks], zt[ft], 0, 0, 0);
+                const int o = (ft * 16 + r16) * (D + 8) + ks * 32 + qg * 8;
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), qf[ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * (D + 8) + o), qf[ks], zt[ft], 0, 0, 0);
             }
         }
         float zmax = -INFINITY, zmin = INFINITY;
@@ -239,56 +299,24 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     const int64_t ws0 = t - w + 1 > 0 ? t - w + 1 : 0;
     const int nWin = w > 0 ? (int)(t - ws0 + 1) : 0;
     const int nK = nWin + cnt;
+    // row of key kidx (0 <= kidx < nK): window position ws0 + kidx (ring slot
+    // (ws0 + kidx) mod w, the newest being this step's token), then cache slot
+    // kidx - nWin; chosen by selects so that a block's loads issue together
+    const int rs0 = w > 0 ? (int)(ws0 % w) : 0;
     auto key_row = [&](int kidx, bool v) -> const bf16* {
-        if (kidx < nWin) {
-            const int64_t p = ws0 + kidx;
-            if (p == t) return v ? vnew : knew;
-            return (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)(p % w) * D;
-        }
-        return (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (size_t)(kidx - nWin) * D;
+        int slot = rs0 + kidx;
+        slot = slot >= w ? slot - w : slot;
+        const bf16* pw = (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)slot * D;
+        const bf16* pc = (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (ptrdiff_t)(kidx - nWin) * D;
+        const bf16* pn = v ? vnew : knew;
+        return kidx < nWin ? (kidx == nWin - 1 ? pn : pw) : pc;
     };
     const float tau = d.tau;
 
     // SRE of 16 candidates whose K^T frags are kb[] (column r16), values read by vfun(dt, i)
     auto sre_tile = [&](const bf16x8* kb, bool colvalid, auto vfun) -> float {
-        floatx4 zt[Fh / 16];
-#pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft) {
-            zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + o), kb[ks], zt[ft], 0, 0, 0);
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + Fh * D + o), kb[ks], zt[ft], 0, 0, 0);
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wb + 2 * Fh * D + o), kb[ks], zt[ft], 0, 0, 0);
-            }
-        }
-        float zmax = -INFINITY, zmin = INFINITY;
-#pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
         float hv[F / 4];
-        float sp = 0.f, sn = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e1 = expf(zt[ft][i] - zmax), e2 = expf(zmin - zt[ft][i]);
-                hv[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
-                hv[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
-                sp += e1;
-                sn += e2;
-            }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
-        const float isp = 1.f / sp, isn = 1.f / sn;
+        phi_tile<D, F>(Wl, kb, r16, qg, hv);
         bf16x8 bh[FM], bl[FM];
         float dd = 0.f;
 #pragma unroll
@@ -296,8 +324,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             u16x8 uh, ul;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int hidx = mf * 8 + j;
-                const float x = hv[hidx] * (hidx < Fh / 4 ? isp : isn);
+                const float x = hv[mf * 8 + j];
                 const uint16_t h = bf16_bits(x);
                 uh[j] = h;
                 ul[j] = bf16_bits(x - bf16_val(h));
@@ -338,16 +365,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     for (int bi = 0; bi < nblk; ++bi) {
         const int base = bi * KBL;
         __syncthreads();  // previous block consumed
-        for (int idx = tid; idx < KBL * (D / 8); idx += 256) {
-            const int kr = idx / (D / 8), un = idx % (D / 8), kidx = base + kr;
-            const uint4 k4 = kidx < nK ? *(const uint4*)(key_row(kidx, false) + un * 8) : make_uint4(0, 0, 0, 0);
-            *(uint4*)(stK + kr * KP + un * 8) = k4;
+        // every load of the block is issued before any is waited for; rows past nK
+        // load the last key and are zeroed
+        // this wave's keys base + wave * KW + tt * 16 + r16 as MFMA fragments, straight
+        // from memory (a lane's 16 bytes are contiguous in the key row)
+        constexpr int VN = (KBL / 2) * (D / 8) / 256;
+        uint4 kq[2][DS], vq0[VN], vq1[VN];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int kidx = base + wave * KW + tt * 16 + r16;
+            const bf16* kr = key_row(kidx < nK ? kidx : nK - 1, false);
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) kq[tt][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
         }
-        for (int idx = tid; idx < (KBL / 2) * (D / 8); idx += 256) {
-            const int pr = idx / (D / 8), un = idx % (D / 8);
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            const int idx = tid + k * 256, k0 = base + 2 * (idx / (D / 8)), un = idx % (D / 8);
+            vq0[k] = *(const uint4*)(key_row(k0 < nK ? k0 : nK - 1, true) + un * 8);
+            vq1[k] = *(const uint4*)(key_row(k0 + 1 < nK ? k0 + 1 : nK - 1, true) + un * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            const int idx = tid + k * 256, pr = idx / (D / 8), un = idx % (D / 8);
             const int k0 = base + 2 * pr, k1 = k0 + 1;
-            const uint4 v0 = k0 < nK ? *(const uint4*)(key_row(k0, true) + un * 8) : make_uint4(0, 0, 0, 0);
-            const uint4 v1 = k1 < nK ? *(const uint4*)(key_row(k1, true) + un * 8) : make_uint4(0, 0, 0, 0);
+            const uint4 v0 = k0 < nK ? vq0[k] : make_uint4(0, 0, 0, 0);
+            const uint4 v1 = k1 < nK ? vq1[k] : make_uint4(0, 0, 0, 0);
             const int kc = (2 * pr / KW) * KW + key_perm((2 * pr) % KW);
             const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
@@ -368,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             sT[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) {
-                kfr[tt][ks] = *(const bf16x8*)(stK + (wave * KW + tt * 16 + r16) * KP + ks * 32 + qg * 8);
+                kfr[tt][ks] = __builtin_bit_cast(bf16x8, kb0 + tt * 16 + r16 < nK ? kq[tt][ks] : make_uint4(0, 0, 0, 0));
                 sT[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[tt][ks], qf[ks], sT[tt], 0, 0, 0);
             }
         }
@@ -492,20 +534,40 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
         __syncthreads();
         victim = misc[0];
-        // phi of the folded key in fp32 (wave 0), then H += phi v^T, s += phi
+        // phi of the folded key (wave 0, column 0 of a tile) and its value (wave 1),
+        // then H += phi v^T, s += phi
         if (wave == 0) {
             const bf16* kr = victim < cnt ? ch.cache_k<bf16>() + (size_t)victim * D : kE;
-            for (int j = lane; j < D; j += 64) xrow[j] = to_f32(kr[j]);
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
-            phi_row_wave<D, Fh>(Wf, xrow, phiF, lane);
+            bf16x8 kb[DS];
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                const uint4 u4 = r16 == 0 ? *(const uint4*)(kr + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+                kb[ks] = __builtin_bit_cast(bf16x8, u4);
+            }
+            float x[F / 4];
+            phi_tile<D, F>(Wl, kb, r16, qg, x);
+            if (r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) phiF[slot_feature(h, qg)] = x[h];
+        } else if (wave == 1) {
+            const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
+            for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
         }
         __syncthreads();
-        const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
         float* Hd = ch.H();
-        for (int i = tid; i < D * F; i += 256) {
-            const int dd = i / F, f = i % F;
-            Hd[i] += to_f32(vr[dd]) * phiF[f];
+        constexpr int HN = D * F / 4 / 256;  // float4 per thread, all loaded before any is stored
+        float4 h4[HN];
+#pragma unroll
+        for (int k = 0; k < HN; ++k) h4[k] = *(const float4*)(Hd + (size_t)(tid + k * 256) * 4);
+#pragma unroll
+        for (int k = 0; k < HN; ++k) {
+            const int i = (tid + k * 256) * 4, dd = i / F, f = i % F;
+            const float vv = xrow[dd];
+            h4[k].x += vv * phiF[f];
+            h4[k].y += vv * phiF[f + 1];
+            h4[k].z += vv * phiF[f + 2];
+            h4[k].w += vv * phiF[f + 3];
+            *(float4*)(Hd + i) = h4[k];
         }
         for (int f = tid; f < F; f += 256) ch.s()[f] += phiF[f];
     }
