@@ -19,6 +19,8 @@
 //             exceed the capacity, and the leaving key takes its cache slot.
 #pragma once
 
+#include <type_traits>
+
 #include "lola_output.h"
 
 namespace lola {
@@ -49,54 +51,78 @@ __host__ __device__ inline DecSmem dec_smem(int D, int F, int C)
     return m;
 }
 
-// phi = [softmax(W k); softmax(-W k)] of the 16 keys of an MFMA tile (key r16 in
-// column r16): z^T = W K^T by MFMA with W in three bf16 parts (exact products
-// against bf16 keys, fp32 sums), then one softmax per half over the features.
-// x[h] is the feature of operand slot h: slot h = 8 mf + j holds feature
-// 16 (2 mf + j / 4) + 4 qg + j % 4 (positive half for mf < F / 64).
-template <int D, int F>
-__device__ __forceinline__ void phi_tile(const uint16_t* Wl, const bf16x8* kb, int r16, int qg, float* x)
+// e^x as 2^(x log2 e): the product is carried in two floats (log2 e split into
+// a float and its remainder, as in Cody and Waite's argument reduction), so the
+// hardware 2^ instruction sees an argument good to about 2^-40 relative and
+// 2^r = 1 + r ln 2 covers the small remainder r.  Arguments here are <= 0.
+__device__ __forceinline__ float exp_acc(float x)
+{
+    constexpr float kL1 = 1.44269502162933349609375f;  // log2(e) rounded to float
+    constexpr float kL2 = 1.9259629911783447e-08f;     // log2(e) - kL1
+    const float t = x * kL1;
+    const float r = fmaf(x, kL1, -t) + x * kL2;
+    return __builtin_amdgcn_exp2f(t) * fmaf(r, 0.693147180559945309f, 1.0f);
+}
+
+// phi = [softmax(W k); softmax(-W k)] of P tiles of 16 keys (key r16 of tile p in
+// column r16 of kb[p]): z^T = W K^T by MFMA with W in three bf16 parts (exact
+// products against bf16 keys, fp32 sums; the W operands are read once for all P
+// tiles), then one softmax per half over the features.  x[p][h] is the feature
+// of operand slot h: slot h = 8 mf + j holds feature 16 (2 mf + j / 4) + 4 qg + j % 4
+// (positive half for mf < F / 64).
+template <int D, int F, int P>
+__device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)[D / 32], int r16, int qg,
+                                          float (*x)[F / 4])
 {
     constexpr int Fh = F / 2, DS = D / 32, WS = D + 8;  // Wl: [3][Fh][WS] in LDS
-    floatx4 zt[Fh / 16];
+    floatx4 zt[P][Fh / 16];
 #pragma unroll
     for (int ft = 0; ft < Fh / 16; ++ft) {
-        zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < P; ++p) zt[p][ft] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) {
             const int o = (ft * 16 + r16) * WS + ks * 32 + qg * 8;
-            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), kb[ks], zt[ft], 0, 0, 0);
-            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * WS + o), kb[ks], zt[ft], 0, 0, 0);
-            zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + 2 * Fh * WS + o), kb[ks], zt[ft], 0, 0, 0);
+            const bf16x8 w0 = *(const bf16x8*)(Wl + o), w1 = *(const bf16x8*)(Wl + Fh * WS + o),
+                         w2 = *(const bf16x8*)(Wl + 2 * Fh * WS + o);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                zt[p][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, kb[p][ks], zt[p][ft], 0, 0, 0);
+                zt[p][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, kb[p][ks], zt[p][ft], 0, 0, 0);
+                zt[p][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, kb[p][ks], zt[p][ft], 0, 0, 0);
+            }
         }
     }
-    float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
-    for (int ft = 0; ft < Fh / 16; ++ft)
+    for (int p = 0; p < P; ++p) {
+        float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-    zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-    zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
-    float sp = 0.f, sn = 0.f;
+        for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
-    for (int ft = 0; ft < Fh / 16; ++ft)
+            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[p][ft][i]); zmin = fminf(zmin, zt[p][ft][i]); }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
+        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        float sp = 0.f, sn = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float e1 = expf(zt[ft][i] - zmax), e2 = expf(zmin - zt[ft][i]);
-            x[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
-            x[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
-            sp += e1;
-            sn += e2;
-        }
-    sp += __shfl_xor(sp, 16, 64);
-    sp += __shfl_xor(sp, 32, 64);
-    sn += __shfl_xor(sn, 16, 64);
-    sn += __shfl_xor(sn, 32, 64);
-    const float isp = 1.f / sp, isn = 1.f / sn;
+        for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
-    for (int h = 0; h < F / 4; ++h) x[h] *= h < Fh / 4 ? isp : isn;
+            for (int i = 0; i < 4; ++i) {
+                const float e1 = exp_acc(zt[p][ft][i] - zmax), e2 = exp_acc(zmin - zt[p][ft][i]);
+                x[p][(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+                x[p][Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+                sp += e1;
+                sn += e2;
+            }
+        sp += __shfl_xor(sp, 16, 64);
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 16, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float isp = 1.f / sp, isn = 1.f / sn;
+#pragma unroll
+        for (int h = 0; h < F / 4; ++h) x[p][h] *= h < Fh / 4 ? isp : isn;
+    }
 }
 
 // feature index of operand slot h (see phi_tile) for lane group qg
@@ -193,11 +219,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             const uint4 u4 = (r16 == 0 && hasE) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
             kb[ks] = __builtin_bit_cast(bf16x8, u4);
         }
-        float x[F / 4];
-        phi_tile<D, F>(Wl, kb, r16, qg, x);
+        float x[1][F / 4];
+        phi_tiles<D, F, 1>(Wl, &kb, r16, qg, x);
         if (r16 == 0)
 #pragma unroll
-            for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[h];
+            for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
     }
     __syncthreads();
 
@@ -313,54 +339,78 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     };
     const float tau = d.tau;
 
-    // SRE of 16 candidates whose K^T frags are kb[] (column r16), values read by vfun(dt, i)
-    auto sre_tile = [&](const bf16x8* kb, bool colvalid, auto vfun) -> float {
-        float hv[F / 4];
-        phi_tile<D, F>(Wl, kb, r16, qg, hv);
-        bf16x8 bh[FM], bl[FM];
-        float dd = 0.f;
+    // SRE of P tiles of 16 candidates (candidate r16 of tile p: key fragments kb[p],
+    // values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p] whether it is one):
+    // n^T = H^T phi^T with H and phi in bf16 hi/lo parts (hi.hi + lo.hi + hi.lo;
+    // the H operands are read once for all P tiles), d = s . phi, e = |n / d - v|^2
+    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e) {
+        constexpr int P = decltype(pTag)::value;
+        bf16x8 bh[P][FM], bl[P][FM];
+        float inv[P];
+        {
+            float x[P][F / 4];
+            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
 #pragma unroll
-        for (int mf = 0; mf < FM; ++mf) {
-            u16x8 uh, ul;
+            for (int p = 0; p < P; ++p) {
+                float dd = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = hv[mf * 8 + j];
-                const uint16_t h = bf16_bits(x);
-                uh[j] = h;
-                ul[j] = bf16_bits(x - bf16_val(h));
-                dd += x * sP[mf * 32 + qg * 8 + j];
+                for (int mf = 0; mf < FM; ++mf) {
+                    u16x8 uh, ul;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float xv = x[p][mf * 8 + j];
+                        const uint16_t h = bf16_bits(xv);
+                        uh[j] = h;
+                        ul[j] = bf16_bits(xv - bf16_val(h));
+                        dd += xv * sP[mf * 32 + qg * 8 + j];
+                    }
+                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
+                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
+                }
+                dd += __shfl_xor(dd, 16, 64);
+                dd += __shfl_xor(dd, 32, 64);
+                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
             }
-            bh[mf] = __builtin_bit_cast(bf16x8, uh);
-            bl[mf] = __builtin_bit_cast(bf16x8, ul);
         }
-        dd += __shfl_xor(dd, 16, 64);
-        dd += __shfl_xor(dd, 32, 64);
-        const float inv = dd > 0.f ? 1.f / dd : 0.f;
-        float e = 0.f;
+        float es[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) es[p] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f}, acc2 = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 acc[P], acc2[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) acc[p] = acc2[p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mf = 0; mf < FM; ++mf) {
                 const int o = (dt * 16 + r16) * HP + mf * 32 + qg * 8;
                 const bf16x8 ah = *(const bf16x8*)(HhT + o);
                 const bf16x8 al = *(const bf16x8*)(HlT + o);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[mf], acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[mf], acc2, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[mf], acc2, 0, 0, 0);
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[p][mf], acc[p], 0, 0, 0);
+                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[p][mf], acc2[p], 0, 0, 0);
+                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[p][mf], acc2[p], 0, 0, 0);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float df = (acc[i] + acc2[i]) * inv - (colvalid ? vfun(dt, i) : 0.f);
-                e += df * df;
+            for (int p = 0; p < P; ++p) {
+                const float vv[4] = {__uint_as_float(vq[p][dt].x << 16), __uint_as_float(vq[p][dt].x & 0xffff0000u),
+                                     __uint_as_float(vq[p][dt].y << 16), __uint_as_float(vq[p][dt].y & 0xffff0000u)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float df = (acc[p][i] + acc2[p][i]) * inv[p] - (cv[p] ? vv[i] : 0.f);
+                    es[p] += df * df;
+                }
             }
         }
-        e += __shfl_xor(e, 16, 64);
-        e += __shfl_xor(e, 32, 64);
-        return e;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            es[p] += __shfl_xor(es[p], 16, 64);
+            es[p] += __shfl_xor(es[p], 32, 64);
+            e[p] = es[p];
+        }
     };
 
-    const bool needSel = hasE && cnt + 1 > C;
     const int nblk = (nK + KBL - 1) / KBL;
     for (int bi = 0; bi < nblk; ++bi) {
         const int base = bi * KBL;
@@ -448,19 +498,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(stVT + (dt * 16 + r16) * VP + wave * KW + qg * 8),
                                                                 pb, O[dt], 0, 0, 0);
         }
-        // SRE of the cached keys among the wave's 32 (only needed when a pair must be folded)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int k16 = kb0 + tt * 16;
-            if (!needSel || k16 + 15 < nWin || k16 >= nK) continue;  // wave-uniform
-            const int kidx = k16 + r16;
-            const bool cv = kidx >= nWin && kidx < nK;
-            const int kl = wave * KW + tt * 16 + r16;  // staged row
-            const int kc = (kl / KW) * KW + key_perm(kl % KW);
-            auto vfun = [&](int dt, int i) -> float { return bf16_val(stVT[(dt * 16 + qg * 4 + i) * VP + kc]); };
-            const float e = sre_tile(kfr[tt], cv, vfun);
-            if (qg == 0 && cv) esc[kidx - nWin] = e;
-        }
     }
 
     // ---- merge the waves' softmax parts, add the linear part, store ----
@@ -494,21 +531,52 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
 
-    // ---- SRE of the leaving key (wave 0), then the pair to fold ----
+    // ---- SRE of the cached pairs and of the leaving pair (only when one must be
+    //      folded): the cache in tiles of 16 slots, then the leaving key as a tile of
+    //      its own, dealt to the waves in turn; each tile's key and value rows are
+    //      loaded while the previous tile is scored ----
     const int nU = cnt + (hasE ? 1 : 0);
-    if (hasE && nU > C && wave == 0) {
-        bf16x8 kb[DS];
+    if (hasE && nU > C) {
+        const int nT = (cnt + 15) / 16;  // tile nT is the leaving key
+        uint4 kq[2][DS];
+        uint2 vq[2][DT];
+        auto tile_load = [&](int p, int tt) {
+            const bool leave = tt == nT;
+            const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
+            const bf16* kr = leave ? kE : ch.cache_k<bf16>() + (size_t)slot * D;
+            const bf16* vr = leave ? vE : ch.cache_v<bf16>() + (size_t)slot * D;
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) {
-            const uint4 u4 = r16 == 0 ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
-            kb[ks] = __builtin_bit_cast(bf16x8, u4);
+            for (int ks = 0; ks < DS; ++ks) kq[p][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vq[p][dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
+        };
+        // the wave's tiles wave, wave + NW, ... two at a time; the next two load
+        // while the current two are scored
+        if (wave <= nT) tile_load(0, wave);
+        if (wave + NW <= nT) tile_load(1, wave + NW);
+        for (int t0 = wave; t0 <= nT; t0 += 2 * NW) {
+            const int tl[2] = {t0, t0 + NW};
+            bf16x8 kb[2][DS];
+            bool cv[2];
+            uint2 vv[2][DT];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                cv[p] = tl[p] == nT ? r16 == 0 : tl[p] * 16 + r16 < cnt;
+#pragma unroll
+                for (int ks = 0; ks < DS; ++ks)
+                    kb[p][ks] = __builtin_bit_cast(bf16x8, cv[p] ? kq[p][ks] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vv[p][dt] = vq[p][dt];
+            }
+            if (t0 + 2 * NW <= nT) tile_load(0, t0 + 2 * NW);
+            if (t0 + 3 * NW <= nT) tile_load(1, t0 + 3 * NW);
+            float e[2];
+            if (tl[1] <= nT) sre_tiles(std::integral_constant<int, 2>{}, kb, cv, vv, e);  // wave-uniform
+            else sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vv, e);
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                if (tl[p] <= nT && qg == 0 && cv[p]) esc[tl[p] == nT ? cnt : tl[p] * 16 + r16] = e[p];
         }
-        float vreg[DT * 4];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) load4(vE + dt * 16 + qg * 4, vreg + dt * 4);
-        auto vfun = [&](int dt, int i) -> float { return vreg[dt * 4 + i]; };
-        const float e = sre_tile(kb, r16 == 0, vfun);
-        if (lane == 0) esc[cnt] = e;
     }
     __syncthreads();
     int victim = -1;
@@ -544,11 +612,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 const uint4 u4 = r16 == 0 ? *(const uint4*)(kr + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
                 kb[ks] = __builtin_bit_cast(bf16x8, u4);
             }
-            float x[F / 4];
-            phi_tile<D, F>(Wl, kb, r16, qg, x);
+            float x[1][F / 4];
+            phi_tiles<D, F, 1>(Wl, &kb, r16, qg, x);
             if (r16 == 0)
 #pragma unroll
-                for (int h = 0; h < F / 4; ++h) phiF[slot_feature(h, qg)] = x[h];
+                for (int h = 0; h < F / 4; ++h) phiF[slot_feature(h, qg)] = x[0][h];
         } else if (wave == 1) {
             const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
             for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
