@@ -212,18 +212,107 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
     __syncthreads();  // W parts and H in LDS
-    if (wave == NW - 1) {  // phi of the leaving key (column 0 of a tile)
-        bf16x8 kb[DS];
+    // SRE of P tiles of 16 candidates (candidate r16 of tile p: key fragments kb[p],
+    // values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p] whether it is one):
+    // n^T = H^T phi^T with H and phi in bf16 hi/lo parts (hi.hi + lo.hi + hi.lo;
+    // the H operands are read once for all P tiles), d = s . phi, e = |n / d - v|^2
+    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
+                         float* phi0 = nullptr) {  // phi0: phi of candidate 0 of tile 0, natural order
+        constexpr int P = decltype(pTag)::value;
+        bf16x8 bh[P][FM], bl[P][FM];
+        float inv[P];
+        {
+            float x[P][F / 4];
+            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
+            if (phi0 && r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) phi0[slot_feature(h, qg)] = x[0][h];
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                float dd = 0.f;
+#pragma unroll
+                for (int mf = 0; mf < FM; ++mf) {
+                    u16x8 uh, ul;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float xv = x[p][mf * 8 + j];
+                        const uint16_t h = bf16_bits(xv);
+                        uh[j] = h;
+                        ul[j] = bf16_bits(xv - bf16_val(h));
+                        dd += xv * sP[mf * 32 + qg * 8 + j];
+                    }
+                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
+                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
+                }
+                dd += __shfl_xor(dd, 16, 64);
+                dd += __shfl_xor(dd, 32, 64);
+                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
+            }
+        }
+        float es[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) es[p] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            floatx4 acc[P], acc2[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) acc[p] = acc2[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mf = 0; mf < FM; ++mf) {
+                const int o = (dt * 16 + r16) * HP + mf * 32 + qg * 8;
+                const bf16x8 ah = *(const bf16x8*)(HhT + o);
+                const bf16x8 al = *(const bf16x8*)(HlT + o);
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[p][mf], acc[p], 0, 0, 0);
+                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[p][mf], acc2[p], 0, 0, 0);
+                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[p][mf], acc2[p], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const float vv[4] = {__uint_as_float(vq[p][dt].x << 16), __uint_as_float(vq[p][dt].x & 0xffff0000u),
+                                     __uint_as_float(vq[p][dt].y << 16), __uint_as_float(vq[p][dt].y & 0xffff0000u)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float df = (acc[p][i] + acc2[p][i]) * inv[p] - (cv[p] ? vv[i] : 0.f);
+                    es[p] += df * df;
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            es[p] += __shfl_xor(es[p], 16, 64);
+            es[p] += __shfl_xor(es[p], 32, 64);
+            e[p] = es[p];
+        }
+    };
+
+    // phi of the leaving key (wave 3, column 0 of a tile) and, when a pair must be
+    // folded, its SRE against the step-start state
+    const int nU = cnt + (hasE ? 1 : 0);
+    if (wave == NW - 1) {
+        bf16x8 kb[1][DS];
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) {
             const uint4 u4 = (r16 == 0 && hasE) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
-            kb[ks] = __builtin_bit_cast(bf16x8, u4);
+            kb[0][ks] = __builtin_bit_cast(bf16x8, u4);
         }
-        float x[1][F / 4];
-        phi_tiles<D, F, 1>(Wl, &kb, r16, qg, x);
-        if (r16 == 0)
+        if (hasE && nU > C) {
+            const bool cv[1] = {r16 == 0};
+            uint2 vq[1][DT];
 #pragma unroll
-            for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
+            for (int dt = 0; dt < DT; ++dt) vq[0][dt] = *(const uint2*)(vE + dt * 16 + qg * 4);
+            float e[1];
+            sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vq, e, phiE);
+            if (lane == 0) esc[cnt] = e[0];
+        } else {
+            float x[1][F / 4];
+            phi_tiles<D, F, 1>(Wl, kb, r16, qg, x);
+            if (r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
+        }
     }
     __syncthreads();
 
@@ -338,78 +427,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         return kidx < nWin ? (kidx == nWin - 1 ? pn : pw) : pc;
     };
     const float tau = d.tau;
-
-    // SRE of P tiles of 16 candidates (candidate r16 of tile p: key fragments kb[p],
-    // values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p] whether it is one):
-    // n^T = H^T phi^T with H and phi in bf16 hi/lo parts (hi.hi + lo.hi + hi.lo;
-    // the H operands are read once for all P tiles), d = s . phi, e = |n / d - v|^2
-    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e) {
-        constexpr int P = decltype(pTag)::value;
-        bf16x8 bh[P][FM], bl[P][FM];
-        float inv[P];
-        {
-            float x[P][F / 4];
-            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                float dd = 0.f;
-#pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    u16x8 uh, ul;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float xv = x[p][mf * 8 + j];
-                        const uint16_t h = bf16_bits(xv);
-                        uh[j] = h;
-                        ul[j] = bf16_bits(xv - bf16_val(h));
-                        dd += xv * sP[mf * 32 + qg * 8 + j];
-                    }
-                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
-                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
-                }
-                dd += __shfl_xor(dd, 16, 64);
-                dd += __shfl_xor(dd, 32, 64);
-                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
-            }
-        }
-        float es[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) es[p] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            floatx4 acc[P], acc2[P];
-#pragma unroll
-            for (int p = 0; p < P; ++p) acc[p] = acc2[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int mf = 0; mf < FM; ++mf) {
-                const int o = (dt * 16 + r16) * HP + mf * 32 + qg * 8;
-                const bf16x8 ah = *(const bf16x8*)(HhT + o);
-                const bf16x8 al = *(const bf16x8*)(HlT + o);
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[p][mf], acc[p], 0, 0, 0);
-                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[p][mf], acc2[p], 0, 0, 0);
-                    acc2[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[p][mf], acc2[p], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const float vv[4] = {__uint_as_float(vq[p][dt].x << 16), __uint_as_float(vq[p][dt].x & 0xffff0000u),
-                                     __uint_as_float(vq[p][dt].y << 16), __uint_as_float(vq[p][dt].y & 0xffff0000u)};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float df = (acc[p][i] + acc2[p][i]) * inv[p] - (cv[p] ? vv[i] : 0.f);
-                    es[p] += df * df;
-                }
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            es[p] += __shfl_xor(es[p], 16, 64);
-            es[p] += __shfl_xor(es[p], 32, 64);
-            e[p] = es[p];
-        }
-    };
 
     const int nblk = (nK + KBL - 1) / KBL;
     for (int bi = 0; bi < nblk; ++bi) {
@@ -531,20 +548,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
 
-    // ---- SRE of the cached pairs and of the leaving pair (only when one must be
-    //      folded): the cache in tiles of 16 slots, then the leaving key as a tile of
-    //      its own, dealt to the waves in turn; each tile's key and value rows are
-    //      loaded while the previous tile is scored ----
-    const int nU = cnt + (hasE ? 1 : 0);
+    // ---- SRE of the cached pairs (only when a pair must be folded; the leaving
+    //      pair's was scored with its phi): the cache in tiles of 16 slots dealt to
+    //      the waves in turn; each tile's key and value rows are loaded while the
+    //      previous tiles are scored ----
     if (hasE && nU > C) {
-        const int nT = (cnt + 15) / 16;  // tile nT is the leaving key
+        const int nT = (cnt + 15) / 16;
         uint4 kq[2][DS];
         uint2 vq[2][DT];
         auto tile_load = [&](int p, int tt) {
-            const bool leave = tt == nT;
             const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
-            const bf16* kr = leave ? kE : ch.cache_k<bf16>() + (size_t)slot * D;
-            const bf16* vr = leave ? vE : ch.cache_v<bf16>() + (size_t)slot * D;
+            const bf16* kr = ch.cache_k<bf16>() + (size_t)slot * D;
+            const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) kq[p][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
 #pragma unroll
@@ -552,30 +567,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         };
         // the wave's tiles wave, wave + NW, ... two at a time; the next two load
         // while the current two are scored
-        if (wave <= nT) tile_load(0, wave);
-        if (wave + NW <= nT) tile_load(1, wave + NW);
-        for (int t0 = wave; t0 <= nT; t0 += 2 * NW) {
+        if (wave < nT) tile_load(0, wave);
+        if (wave + NW < nT) tile_load(1, wave + NW);
+        for (int t0 = wave; t0 < nT; t0 += 2 * NW) {
             const int tl[2] = {t0, t0 + NW};
             bf16x8 kb[2][DS];
             bool cv[2];
             uint2 vv[2][DT];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                cv[p] = tl[p] == nT ? r16 == 0 : tl[p] * 16 + r16 < cnt;
+                cv[p] = tl[p] * 16 + r16 < cnt;
 #pragma unroll
                 for (int ks = 0; ks < DS; ++ks)
                     kb[p][ks] = __builtin_bit_cast(bf16x8, cv[p] ? kq[p][ks] : make_uint4(0, 0, 0, 0));
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vv[p][dt] = vq[p][dt];
             }
-            if (t0 + 2 * NW <= nT) tile_load(0, t0 + 2 * NW);
-            if (t0 + 3 * NW <= nT) tile_load(1, t0 + 3 * NW);
+            if (t0 + 2 * NW < nT) tile_load(0, t0 + 2 * NW);
+            if (t0 + 3 * NW < nT) tile_load(1, t0 + 3 * NW);
             float e[2];
-            if (tl[1] <= nT) sre_tiles(std::integral_constant<int, 2>{}, kb, cv, vv, e);  // wave-uniform
+            if (tl[1] < nT) sre_tiles(std::integral_constant<int, 2>{}, kb, cv, vv, e);  // wave-uniform
             else sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vv, e);
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                if (tl[p] <= nT && qg == 0 && cv[p]) esc[tl[p] == nT ? cnt : tl[p] * 16 + r16] = e[p];
+                if (tl[p] < nT && qg == 0 && cv[p]) esc[tl[p] * 16 + r16] = e[p];
         }
     }
     __syncthreads();
