@@ -3,7 +3,8 @@
 // One workgroup (8 waves) handles 128 query rows of one (interval, chain);
 // each wave owns 16 rows as one 16-column MFMA tile (the queries are the
 // columns, so softmax statistics live in the lanes).  Per workgroup:
-//   - H_c^T (bf16, features in operand order) and W (bf16 hi + lo) staged once;
+//   - H_c^T (bf16, features in operand order) and W (bf16 hi + lo) staged in LDS
+//     once (every load issued before any is waited for);
 //   - z^T = W Q^T gives phi(q) (two softmax halves over the features),
 //     O^T = H_c^T phi(q)^T and Z = s_c . phi(q) start the accumulators
 //     (linear read of the interval-start state, LoLA summary section
@@ -26,7 +27,7 @@ constexpr int kKeyBlock = 32;
 constexpr int kOutThreads = 512;  // 8 waves x 16 query rows
 
 struct OutSmem {
-    size_t sP, refs, Ks, VT, Pk, total;
+    size_t sP, refs, Wl, Hs, Ks, VT, Pk, total;
 };
 
 __host__ __device__ inline OutSmem out_smem(int D, int F, int C)
@@ -35,6 +36,8 @@ __host__ __device__ inline OutSmem out_smem(int D, int F, int C)
     size_t off = 0;
     m.sP = off;   off += align_up(sizeof(float) * F, 16);
     m.refs = off; off += align_up(sizeof(int) * (size_t)(C > 0 ? C : 1), 16);
+    m.Wl = off;   off += align_up(sizeof(uint16_t) * 2 * (size_t)(F / 2) * (D + 8), 16);  // W hi, lo [2][Fh][D+8]
+    m.Hs = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);            // H_c^T [D][F+8]
     m.Ks = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (D + 8);
     m.VT = off;   off += sizeof(uint16_t) * (size_t)D * (kKeyBlock + 8);
     m.Pk = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (F + 8);
@@ -59,6 +62,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     uint16_t* Ks = (uint16_t*)(smem + sm.Ks);
     uint16_t* VT = (uint16_t*)(smem + sm.VT);
     uint16_t* Pk = (uint16_t*)(smem + sm.Pk);
+    uint16_t* Wl = (uint16_t*)(smem + sm.Wl);
+    uint16_t* Hs = (uint16_t*)(smem + sm.Hs);
 
     const int G = d.G, L = d.L, w = d.w;
     const int chain = blockIdx.y, b = chain / d.Hkv, g = chain % d.Hkv;
@@ -75,8 +80,23 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     // ---- stage s_c (operand order) and the cache refs of the snapshot ----
     const uint16_t* HTg = (const uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D;  // [D][F] bf16
     const uint16_t* Whg = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;          // [Fh][D]
-    const uint16_t* Wlg = Whg + (size_t)Fh * D;
     {
+        constexpr int WN = 2 * Fh * D / 8 / NT, HN = D * F / 8 / NT;  // 16-byte pieces per thread
+        uint4 w4[WN], h4[HN];
+#pragma unroll
+        for (int k = 0; k < WN; ++k) w4[k] = *(const uint4*)(Whg + (size_t)(tid + k * NT) * 8);
+#pragma unroll
+        for (int k = 0; k < HN; ++k) h4[k] = *(const uint4*)(HTg + (size_t)(tid + k * NT) * 8);
+#pragma unroll
+        for (int k = 0; k < WN; ++k) {
+            const int e = (tid + k * NT) * 8;  // row = part * Fh + feature
+            *(uint4*)(Wl + (e / D) * (D + 8) + e % D) = w4[k];
+        }
+#pragma unroll
+        for (int k = 0; k < HN; ++k) {
+            const int e = (tid + k * NT) * 8;
+            *(uint4*)(Hs + (e / F) * (F + 8) + e % F) = h4[k];
+        }
         const float* sS = (const float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
         for (int i = tid; i < F; i += NT) sP[perm_pos(i)] = sS[i];
         const int Cp0 = d.C > 0 ? d.C : 1;
@@ -117,9 +137,9 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) {
-                const int o = (ft * 16 + r16) * D + ks * 32 + qg * 8;
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Whg + o), qf[rt][ks], zt[ft], 0, 0, 0);
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wlg + o), qf[rt][ks], zt[ft], 0, 0, 0);
+                const int o = (ft * 16 + r16) * (D + 8) + ks * 32 + qg * 8;
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), qf[rt][ks], zt[ft], 0, 0, 0);
+                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * (D + 8) + o), qf[rt][ks], zt[ft], 0, 0, 0);
             }
         }
         float zmax = -INFINITY, zmin = INFINITY;
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         for (int rt = 0; rt < RT; ++rt) O[rt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mf = 0; mf < FM; ++mf) {
-            const bf16x8 ha = *(const bf16x8*)(HTg + (size_t)(dt * 16 + r16) * F + mf * 32 + qg * 8);
+            const bf16x8 ha = *(const bf16x8*)(Hs + (dt * 16 + r16) * (F + 8) + mf * 32 + qg * 8);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pf[rt][mf], O[rt][dt], 0, 0, 0);
         }
