@@ -9,7 +9,7 @@
 //     O^T = H_c^T phi(q)^T and Z = s_c . phi(q) start the accumulators
 //     (linear read of the interval-start state, LoLA summary section
 //     "Inferentiestrategie", step 4);
-//   - keys in blocks of 32 (the window span of the interval, then the cache
+//   - keys in blocks of 64 (the window span of the interval, then the cache
 //     snapshot): K, V^T and phi(K) are staged in LDS with 16-byte loads, the
 //     next block prefetched into registers; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
 //     for keys that left the window inside the interval, online softmax with
@@ -23,7 +23,7 @@
 namespace lola {
 
 constexpr int kOutRows = 128;  // query rows per workgroup
-constexpr int kKeyBlock = 32;
+constexpr int kKeyBlock = 64;
 constexpr int kOutThreads = 512;  // 8 waves x 16 query rows
 
 struct OutSmem {
@@ -45,7 +45,7 @@ __host__ __device__ inline OutSmem out_smem(int D, int F, int C)
     return m;
 }
 
-// position of key k (0..31) of a block in the P^T / V^T operand order
+// position of key k (0..31) of a 32-key half block in the P^T / V^T operand order
 __device__ __forceinline__ int key_perm(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
 
 template <int D, int F>
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             if (idx < KB * D / 8) *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
         }
         if (tid < VPU) {
-            // keys 2pr, 2pr+1 sit next to each other in the operand order
-            const int pr = tid / (D / 8), un = tid % (D / 8), kc = key_perm(2 * pr);
+            // keys 2pr, 2pr+1 sit next to each other in the operand order of their half
+            const int pr = tid / (D / 8), un = tid % (D / 8), kc = (2 * pr / 32) * 32 + key_perm((2 * pr) % 32);
             const uint32_t w0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w}, w1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -277,9 +277,10 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB);
         const bool anyPend = base < nSpan && sp0 + base <= lastPend;
 
-        floatx4 sT[RT][2], kT[RT][2];
+        constexpr int KT = KB / 16;  // key tiles per block
+        floatx4 sT[RT][KT], kT[RT][KT];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < KT; ++tt) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = kT[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -297,17 +298,19 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                 }
             }
         }
-        bf16x8 pb[RT];
+        bf16x8 pb[RT][KB / 32];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            // the lane's 8 keys: base + tt*16 + qg*4 + i, operand slot j = tt*4 + i
-            float lg[8];
-            int kind[8];
+            // the lane's KB/4 keys: base + tt*16 + qg*4 + i (tt = j / 4, i = j % 4); key j
+            // sits in slot j % 8 of the P^T operand of half j / 8
+            constexpr int NJ = KB / 4;
+            float lg[NJ];
+            int kind[NJ];
             float bmax = -INFINITY;
             // query position relative to the span start; span key kidx sits at sp0 + kidx
             const int tr = qv[rt] ? (int)(tq[rt] - sp0) : -1;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int tt = j >> 2, i = j & 3;
                 const int kidx = base + tt * 16 + qg * 4 + i;
                 int kd = 0;
@@ -331,25 +334,31 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
             Zp[rt] *= resc;
             const float elin = __expf(-mnew);
-            u16x8 u;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int tt = j >> 2, i = j & 3;
-                float pv_ = 0.f;
-                if (kind[j] == 1) pv_ = __expf(lg[j] - mnew);
-                else if (kind[j] == 2) pv_ = kT[rt][tt][i] * elin;
-                Zp[rt] += pv_;
-                u[j] = bf16_bits(pv_);
+            for (int hh = 0; hh < KB / 32; ++hh) {
+                u16x8 u;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int j = hh * 8 + jj, tt = j >> 2, i = j & 3;
+                    float pv_ = 0.f;
+                    if (kind[j] == 1) pv_ = __expf(lg[j] - mnew);
+                    else if (kind[j] == 2) pv_ = kT[rt][tt][i] * elin;
+                    Zp[rt] += pv_;
+                    u[jj] = bf16_bits(pv_);
+                }
+                pb[rt][hh] = __builtin_bit_cast(bf16x8, u);
             }
-            pb[rt] = __builtin_bit_cast(bf16x8, u);
         }
         // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + qg * 8);
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], O[rt][dt], 0, 0, 0);
-        }
+            for (int hh = 0; hh < KB / 32; ++hh) {
+                const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + hh * 32 + qg * 8);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt][hh], O[rt][dt], 0, 0, 0);
+            }
     }
 
 #undef LOLA_OUT_PREFETCH
