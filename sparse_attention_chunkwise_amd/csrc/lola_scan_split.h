@@ -50,9 +50,9 @@ struct SplitSmem {
 __host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
 {
     SplitSmem m;
-    const int U = C + L, Cp = C > 0 ? C : 1, EP = kFoldChunk + 8, PRS = 2 * F + 8;
+    const int U = C + L, Cp = C > 0 ? C : 1, EP = kFoldChunk + 8;
     size_t off = 0;
-    m.PR = off;     off += align_up(sizeof(uint16_t) * kFoldChunk * (size_t)PRS, 16);  // [EC][PRS]
+    m.PR = off;     off += align_up(sizeof(uint16_t) * 2 * (size_t)F * EP, 16);        // [2F][EP]
     m.VS = off;     off += align_up(sizeof(uint16_t) * 16 * (size_t)EP, 16);          // [16][EP]
     m.AX = off;     off += align_up(sizeof(uint16_t) * 2 * 16 * (size_t)(F + 8), 16); // [2][16][F+8]
     m.s = off;      off += align_up(sizeof(float) * F, 16);
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 {
     constexpr int KW = D / 16, NT = kSplitThreads, NW = NT / 64, FT = F / 16, FM = F / 32;
     constexpr int EC = kFoldChunk, EP = EC + 8, AXS = F + 8, GR = kSplitGroup, NCH = kSelChunks;
-    constexpr int PRS = 2 * F + 8, RES = NW * GR, HT = (FT + NW - 1) / NW;
-    static_assert(EC * 4 == NT && (EC * (2 * F / 8)) % NT == 0, "fold staging covers the chunk exactly");
+    constexpr int RES = NW * GR, HT = (FT + NW - 1) / NW;
+    static_assert(EC * 4 == NT && EC == 64 && (2 * F / 8) % (2 * NW) == 0, "fold staging covers the chunk exactly");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     if (chain >= chains) return;  // the whole chain is absent: none of its blocks waits
     const int col0 = 16 * jw;
     const SplitSmem sm = split_smem(F, C, L);
-    uint16_t* PR = (uint16_t*)(smem + sm.PR);      // folded pairs: phi hi | lo (operand order) per row
+    uint16_t* PR = (uint16_t*)(smem + sm.PR);      // folded pairs transposed: row = phi hi | lo slot, column = pair
     uint16_t* VS = (uint16_t*)(smem + sm.VS);      // folded pairs' values, this block's 16 columns, transposed
     uint16_t* AX = (uint16_t*)(smem + sm.AX);      // hi, lo of H^T rows col0.. (operand order)
     float* sP = (float*)(smem + sm.s);             // s, operand order
@@ -585,38 +585,50 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int ve1 = tid >> 2, vq4 = (tid & 3) * 4;  // EC * 4 == NT value pieces
         uint4 t4[SPT];
         uint2 t2;
-        // Rows past the chunk end load the chunk's last pair and are zeroed after the
+        // Lane l of wave w stages pairs 2 (l % 32) and 2 (l % 32) + 1, 16-byte column
+        // groups cg = 2 w + l / 32 + 2 NW m, and writes them transposed (one dword =
+        // one slot of the two pairs, consecutive lanes on consecutive dwords).  Rows
+        // past the chunk end load the chunk's last pair and are zeroed after the
         // load, so that every lookup and load is issued without a branch.
+        constexpr int CG = SPT / 2;  // column groups per lane
+        const int rp = lane & 31, cg0 = 2 * wave + (lane >> 5);
         auto stage_load = [&](int e0) {
             const int ne = nF - e0 < EC ? nF - e0 : EC;  // >= 1
-            int code[SPT];
-#pragma unroll
-            for (int k = 0; k < SPT; ++k) {
-                const int e1 = (tid + k * NT) / (2 * F / 8);
-                code[k] = foldc[e0 + (e1 < ne ? e1 : ne - 1)];
-            }
+            const int c0 = foldc[e0 + (2 * rp < ne ? 2 * rp : ne - 1)];
+            const int c1 = foldc[e0 + (2 * rp + 1 < ne ? 2 * rp + 1 : ne - 1)];
             const int vcode = foldc[e0 + (ve1 < ne ? ve1 : ne - 1)];
             const uint2 y = *(const uint2*)(code_v(vcode) + col0 + vq4);
+            const uint16_t* p0 = code_phs(c0);
+            const uint16_t* p1 = code_phs(c1);
             uint4 x[SPT];
 #pragma unroll
-            for (int k = 0; k < SPT; ++k) {
-                const int c8 = ((tid + k * NT) % (2 * F / 8)) * 8;
-                x[k] = *(const uint4*)(code_phs(code[k]) + c8);
+            for (int m = 0; m < CG; ++m) {
+                const int c8 = (cg0 + 2 * NW * m) * 8;
+                x[2 * m] = *(const uint4*)(p0 + c8);
+                x[2 * m + 1] = *(const uint4*)(p1 + c8);
             }
+            const uint32_t k0 = 2 * rp < ne ? 0xffffffffu : 0u, k1 = 2 * rp + 1 < ne ? 0xffffffffu : 0u;
 #pragma unroll
-            for (int k = 0; k < SPT; ++k) {
-                const int e1 = (tid + k * NT) / (2 * F / 8);
-                const uint32_t keep = e1 < ne ? 0xffffffffu : 0u;
-                t4[k] = make_uint4(x[k].x & keep, x[k].y & keep, x[k].z & keep, x[k].w & keep);
+            for (int m = 0; m < CG; ++m) {
+                t4[2 * m] = make_uint4(x[2 * m].x & k0, x[2 * m].y & k0, x[2 * m].z & k0, x[2 * m].w & k0);
+                t4[2 * m + 1] = make_uint4(x[2 * m + 1].x & k1, x[2 * m + 1].y & k1, x[2 * m + 1].z & k1,
+                                           x[2 * m + 1].w & k1);
             }
             const uint32_t vkeep = ve1 < ne ? 0xffffffffu : 0u;
             t2 = make_uint2(y.x & vkeep, y.y & vkeep);
         };
         auto stage_store = [&]() {
 #pragma unroll
-            for (int k = 0; k < SPT; ++k) {
-                const int idx = tid + k * NT, e1 = idx / (2 * F / 8), c8 = (idx % (2 * F / 8)) * 8;
-                *(uint4*)(PR + e1 * PRS + c8) = t4[k];
+            for (int m = 0; m < CG; ++m) {
+                const int c8 = (cg0 + 2 * NW * m) * 8;
+                const uint32_t a4[4] = {t4[2 * m].x, t4[2 * m].y, t4[2 * m].z, t4[2 * m].w};
+                const uint32_t b4[4] = {t4[2 * m + 1].x, t4[2 * m + 1].y, t4[2 * m + 1].z, t4[2 * m + 1].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = (a4[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                    const uint32_t hi = (b4[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                    *(uint32_t*)(PR + (c8 + j) * EP + 2 * rp) = lo | (hi << 16);
+                }
             }
             VS[(vq4 + 0) * EP + ve1] = (uint16_t)(t2.x & 0xffffu);
             VS[(vq4 + 1) * EP + ve1] = (uint16_t)(t2.x >> 16);
@@ -634,15 +646,9 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 floatx4 sa = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < EC / 32; ++ks) {
-                    u16x8 ph, pl;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint16_t* row = PR + (ks * 32 + qg * 8 + j) * PRS;
-                        ph[j] = row[pos];
-                        pl[j] = row[F + pos];
-                    }
+                    const bf16x8 hb = *(const bf16x8*)(PR + pos * EP + ks * 32 + qg * 8);
+                    const bf16x8 lb = *(const bf16x8*)(PR + (F + pos) * EP + ks * 32 + qg * 8);
                     const bf16x8 bv = *(const bf16x8*)(VS + r16 * EP + ks * 32 + qg * 8);
-                    const bf16x8 hb = __builtin_bit_cast(bf16x8, ph), lb = __builtin_bit_cast(bf16x8, pl);
                     Hacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hb, bv, Hacc[h], 0, 0, 0);
                     Hacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lb, bv, Hacc[h], 0, 0, 0);
                     sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hb, ones, sa, 0, 0, 0);
