@@ -301,6 +301,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     };
 
     uint32_t arrivals = 0;  // exchanges this block has completed
+    uint32_t tauPrev = 0u;  // threshold of the previous selection (wave 0)
     int cur = 0;            // candidate list of this interval: ucodeb + cur * U
     // Operands of the next SRE when each wave has at most two tiles, loaded while
     // the previous interval folds.  A lane keeps the candidate code of the row it
@@ -478,29 +479,63 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     km[i] = (!needSel && nU <= C) ? vm[i] : 0ull;
                 }
                 if (needSel) {
-                    // Threshold bit by bit (SRE >= 0: bit 31 is clear): the largest t with
-                    // #{key >= t} >= C.  Slots past nU hold 0 and never count for t > 0.
-                    // Stop early once exactly C keys reach the threshold.
-                    // (tau, t and the counts are wave-uniform; readfirstlane keeps them scalar)
-                    uint32_t tau = 0u;
-                    int bit = 30, ge = 0;
-                    // kept as a loop: unrolled, its 31 steps would stream through the
-                    // instruction cache once per interval
-#pragma nounroll
-                    do {
-                        const uint32_t t = __builtin_amdgcn_readfirstlane(tau | (1u << bit));
+                    // Threshold: the largest t with #{key >= t} >= C (keys are SRE bit
+                    // patterns, order-preserving since SRE >= 0; slots past nU hold 0).
+                    // The bracket lo < hi keeps count(lo) >= C > count(hi).  It starts
+                    // from the previous interval's threshold, widens by steps that grow
+                    // 4x until it encloses the new one, then narrows at the point where
+                    // the count is expected to cross C (linear in the bit pattern), with
+                    // a halving step whenever two steps did not halve the bracket.  It
+                    // stops once exactly C keys reach lo, or when hi = lo + 1 (then lo
+                    // is the C-th largest key).  lo, hi and the counts are wave-uniform.
+                    uint32_t lo = 0u, hi = 0x80000000u;  // no non-negative pattern reaches hi
+                    int clo = nU, chi = 0;
+                    auto probe = [&](uint32_t t) -> int {
                         uint64_t bal[NC];  // all compares first, then the counts
 #pragma unroll
                         for (int i = 0; i < NC; ++i) bal[i] = __ballot(key[i] >= t);
-                        ge = 0;
+                        int cc = 0;
 #pragma unroll
-                        for (int i = 0; i < NC; ++i) ge += __popcll(bal[i]);
-                        ge = __builtin_amdgcn_readfirstlane(ge);
-                        tau = ge >= C ? t : tau;
-                        bit = __builtin_amdgcn_readfirstlane(bit - 1);
-                    } while (bit >= 0 && ge != C);
+                        for (int i = 0; i < NC; ++i) cc += __popcll(bal[i]);
+                        cc = __builtin_amdgcn_readfirstlane(cc);
+                        if (cc >= C) {
+                            lo = t;
+                            clo = cc;
+                        } else {
+                            hi = t;
+                            chi = cc;
+                        }
+                        return cc;
+                    };
+                    int cc = probe(tauPrev > 0u && tauPrev < hi ? tauPrev : 0x3f800000u);
+                    uint32_t step = 1u << 18;
+#pragma nounroll
+                    while (cc != C && hi - lo > 2u * step) {
+                        cc = probe(cc >= C ? lo + step : hi - step);
+                        step = step < (1u << 28) ? step << 2 : step;
+                    }
+                    uint32_t wprev = 0xffffffffu;
+                    int k = 0;
+#pragma nounroll
+                    while (cc != C && hi - lo > 1u) {
+                        const uint32_t wd = hi - lo;
+                        uint32_t t;
+                        if ((k & 1) && wd > wprev / 2u)
+                            t = lo + wd / 2u;
+                        else {
+                            const float frac = ((float)(clo - C) + 0.5f) * __builtin_amdgcn_rcpf((float)(clo - chi));
+                            t = lo + (uint32_t)((float)wd * frac);
+                            t = t <= lo ? lo + 1u : (t >= hi ? hi - 1u : t);
+                            t = __builtin_amdgcn_readfirstlane(t);
+                        }
+                        if (!(k & 1)) wprev = wd;
+                        ++k;
+                        cc = probe(t);
+                    }
+                    uint32_t tau = lo;
+                    const int ge = clo;
+                    tauPrev = lo;
                     const bool exact = ge == C;
-                    tau = __builtin_amdgcn_readfirstlane(tau);
                     int above = 0, ties = 0;
                     if (!exact) {
 #pragma unroll
