@@ -308,7 +308,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     // holds per tile (pfcode): cache slots mostly keep their pair from one interval
     // to the next and a tile always maps to the same wave, so only rows whose code
     // changed are loaded again.  Where the next SRE is not needed or loads its own
-    // operands, the row of candidate code 0 (extended row 0, always present) is held.
+    // operands, and in a wave's tile slot past the last tile (its results are not
+    // stored), the row of candidate code 0 (extended row 0, always present) is held.
     using Two = std::integral_constant<int, 2>;
     uint4 pfh[2][FM], pfl[2][FM];
     uint2 pfv[2];
@@ -319,12 +320,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int T = (nUq + 15) / 16;
         int code[2];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            int t = ju + PU * (wave + k * NW);
-            t = t < T ? t : T - 1;
+        for (int k = 0; k < 2; ++k) {  // a tile slot past the last tile holds the code-0 row
+            const int t = ju + PU * (wave + k * NW);
             int u = t * 16 + r16;
             u = u < nUq ? u : nUq - 1;
-            code[k] = use ? uc[u] : 0;
+            code[k] = use && t < T ? uc[u] : 0;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k)
@@ -356,18 +356,23 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 
         // ---- interval-start snapshot: H^T hi parts of this block's rows, s and cache
         //      refs (written before the fold and the selection change them) ----
+        // (the blocks of a column slice hold identical rows, and every block the
+        // same s and slot codes, so the writes are spread: block ju writes the
+        // 32-feature pieces m with m % PU == ju, two other blocks s and the refs)
         auto snapshot = [&]() {
-            if (lead && wave == 0) {
+            if (wave == 0) {
                 uint16_t* dst = (uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D +
                                 (size_t)(col0 + r16) * F + qg * 8;
 #pragma unroll
                 for (int m = 0; m < FM; ++m)
-                    *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
+                    if (m % PU == ju) *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
             }
-            if (lead && jw == 0) {
+            if (jw == 1 % KW && ju == 1 % PU) {
                 float* snapS = (float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
-                int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
                 for (int i = tid; i < F; i += NT) snapS[i] = sP[perm_pos(i)];
+            }
+            if (jw == 2 % KW && ju == 2 % PU) {
+                int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
                 for (int i = tid; i < cnt; i += NT) snapRef[i] = cref[i];
                 if (tid == 0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
             }
