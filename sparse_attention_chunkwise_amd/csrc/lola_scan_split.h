@@ -44,7 +44,7 @@ constexpr int kSelChunks = (kMaxCand + 63) / 64;      // 64-candidate chunks a w
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 struct SplitSmem {
-    size_t PR, VS, AX, s, sparts, ebits, foldc, ucode, cref, cpos, freed, tiep, misc, total;
+    size_t PR, VS, AX, s, sparts, ebits, foldc, cref, cpos, freed, tiep, misc, total;
 };
 
 __host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
@@ -59,7 +59,6 @@ __host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
     m.sparts = off; off += align_up(sizeof(uint16_t) * 3 * (size_t)F, 16);            // [3][F]
     m.ebits = off;  off += sizeof(uint32_t) * U;
     m.foldc = off;  off += sizeof(int) * U;
-    m.ucode = off;  off += sizeof(int) * 2 * U;
     m.cref = off;   off += sizeof(int) * Cp;
     m.cpos = off;   off += sizeof(int) * Cp;
     m.freed = off;  off += sizeof(int) * Cp;
@@ -109,7 +108,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     uint16_t* sParts = (uint16_t*)(smem + sm.sparts);
     uint32_t* ebits = (uint32_t*)(smem + sm.ebits);
     int* foldc = (int*)(smem + sm.foldc);          // fold index -> candidate code
-    int* ucodeb = (int*)(smem + sm.ucode);         // two candidate lists (this interval, next)
     int* cref = (int*)(smem + sm.cref);
     int* cpos = (int*)(smem + sm.cpos);
     int* freed = (int*)(smem + sm.freed);
@@ -226,11 +224,16 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         return v;
     };
 
+    // Candidate u of an interval whose cache holds cntq pairs and whose leaving keys
+    // start at extended row xq: the pair in slot u (u < cntq), else leaving key u - cntq.
+    // Codes: >= 0 an extended row of this call, < 0 slot -code - 1 of the call-start cache.
+    auto cand_code = [&](int u, int cntq, int xq) -> int { return u < cntq ? cref[u] : xq + (u - cntq); };
+
     // Partial SRE of this block's candidate tiles t = ju + PU * i, i = ibase + wave +
     // NW * k (k < G): sre_load fetches the phi rows (hi, lo) and the values of a
     // wave's G tiles, sre_math computes them two at a time and publishes the
     // partial errors.
-    auto sre_load = [&](auto gTag, const int* uc, int nUq, int ibase, uint4 (&fh)[decltype(gTag)::value][FM],
+    auto sre_load = [&](auto gTag, int cntq, int xq, int nUq, int ibase, uint4 (&fh)[decltype(gTag)::value][FM],
                         uint4 (&fl)[decltype(gTag)::value][FM], uint2 (&fv)[decltype(gTag)::value]) {
         constexpr int G = decltype(gTag)::value;
         const int T = (nUq + 15) / 16;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             t = t < T ? t : T - 1;
             int u = t * 16 + r16;
             u = u < nUq ? u : nUq - 1;
-            const int code = uc[u];
+            const int code = cand_code(u, cntq, xq);
             const uint16_t* p = code_phs(code) + qg * 8;
 #pragma unroll
             for (int m = 0; m < FM; ++m) {
@@ -302,7 +305,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 
     uint32_t arrivals = 0;  // exchanges this block has completed
     uint32_t tauPrev = 0u;  // threshold of the previous selection (wave 0)
-    int cur = 0;            // candidate list of this interval: ucodeb + cur * U
     // Operands of the next SRE when each wave has at most two tiles, loaded while
     // the previous interval folds.  A lane keeps the candidate code of the row it
     // holds per tile (pfcode): cache slots mostly keep their pair from one interval
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     uint2 pfv[2];
     int pfcode[2] = {INT_MIN, INT_MIN};
     auto tiles_of_block = [&](int nUq) { const int T = (nUq + 15) / 16; return T > ju ? (T - ju + PU - 1) / PU : 0; };
-    auto prefetch_next = [&](int nUq, const int* uc) {
+    auto prefetch_next = [&](int nUq, int cntq, int xq) {
         const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW;
         const int T = (nUq + 15) / 16;
         int code[2];
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             const int t = ju + PU * (wave + k * NW);
             int u = t * 16 + r16;
             u = u < nUq ? u : nUq - 1;
-            code[k] = use && t < T ? uc[u] : 0;
+            code[k] = use && t < T ? cand_code(u, cntq, xq) : 0;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k)
@@ -341,9 +343,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     };
     {
         const Iv v0 = interval(0);
-        for (int u = tid; u < cnt + v0.nE; u += NT) ucodeb[u] = u < cnt ? cref[u] : v0.xE0 + (u - cnt);
-        lds_sync();
-        prefetch_next(cnt + v0.nE, ucodeb);
+        prefetch_next(cnt + v0.nE, cnt, v0.xE0);
     }
 
     for (int c = 0; c < NI; ++c) {
@@ -352,7 +352,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int nE = iv.nE, xE0 = iv.xE0;
         const int nU = cnt + nE;
         const int T = (nU + 15) / 16;
-        const int* ucode = ucodeb + cur * U;
 
         // ---- interval-start snapshot: H^T hi parts of this block's rows, s and cache
         //      refs (written before the fold and the selection change them) ----
@@ -397,7 +396,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     for (int ib = 0; ib < TB; ib += RES) {
                         uint4 fh[GR][FM], fl[GR][FM];
                         uint2 fv[GR];
-                        sre_load(std::integral_constant<int, GR>{}, ucode, nU, ib, fh, fl, fv);
+                        sre_load(std::integral_constant<int, GR>{}, cnt, xE0, nU, ib, fh, fl, fv);
                         sre_math(std::integral_constant<int, GR>{}, nU, ib, xw, tag, Ah, Al, As, fh, fl, fv);
                     }
             }
@@ -466,7 +465,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int cntN = nU < C ? nU : C;
         const Iv ivN = interval(c + 1 < NI ? c + 1 : c);
         const int nUN = c + 1 < NI ? cntN + ivN.nE : 0;
-        int* ucodeN = ucodeb + (cur ^ 1) * U;
         if (wave == 0) {
             auto cand_pos = [&](int u) -> int { return u < cnt ? cpos[u] : (int)(eS + (u - cnt)); };
             // NC = candidate chunks of 64 held per lane (a compile-time bound >= ceil(nU / 64))
@@ -479,7 +477,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 for (int i = 0; i < NC; ++i) {
                     const int u = i * 64 + lane;
                     key[i] = (needSel && u < nU) ? ebits[u] : 0u;
-                    ucv[i] = u < nU ? ucode[u] : 0;
+                    ucv[i] = u < nU ? cand_code(u, cnt, xE0) : 0;
                     vm[i] = __ballot(u < nU);
                     km[i] = (!needSel && nU <= C) ? vm[i] : 0ull;
                 }
@@ -612,8 +610,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             else if (nch <= 5) select_compact(std::integral_constant<int, 5>{});
             else if (nch <= 10) select_compact(std::integral_constant<int, 10>{});
             else select_compact(std::integral_constant<int, NCH>{});
-            lds_wait();
-            for (int u = lane; u < nUN; u += 64) ucodeN[u] = u < cntN ? cref[u] : ivN.xE0 + (u - cntN);
         }
         lds_sync();
         const int nF = misc[5];
@@ -705,7 +701,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         }
         // the next interval's SRE operands, issued once the first chunk is staged (so
         // that they do not queue ahead of its loads); they arrive during the fold
-        prefetch_next(nUN, ucodeN);
+        prefetch_next(nUN, cntN, ivN.xE0);
         if (nF > 0) {
             lds_sync();
             fold_mma();
@@ -741,7 +737,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             }
         }
         lds_sync();
-        cur ^= 1;
         cnt = cntN;
     }
 
