@@ -429,15 +429,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                         ok = 0;
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(1);
+                    // read every slot again (a ready slot keeps its value until exchange k + 2)
 #pragma unroll
                     for (int jj = 0; jj < KW; ++jj) {
-                        if ((uint32_t)(va[jj] >> 32) != tag)
-                            va[jj] = __hip_atomic_load(&xr[(size_t)jj * U + u0], __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                        if ((uint32_t)(vb[jj] >> 32) != tag)
-                            vb[jj] = __hip_atomic_load(&xr[(size_t)jj * U + u1], __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
+                        va[jj] = __hip_atomic_load(&xr[(size_t)jj * U + u0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        vb[jj] = __hip_atomic_load(&xr[(size_t)jj * U + u1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
                 if (!ok) break;
