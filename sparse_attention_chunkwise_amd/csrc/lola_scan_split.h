@@ -229,6 +229,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     // Codes: >= 0 an extended row of this call, < 0 slot -code - 1 of the call-start cache.
     auto cand_code = [&](int u, int cntq, int xq) -> int { return u < cntq ? cref[u] : xq + (u - cntq); };
 
+    // Tiles of the prefetched path (at most 2 NW - 1 per block): block tile i = wave
+    // in slot 0, and i = NW + wave - 1 in slot 1 for waves 1.. (wave 0 runs the
+    // selection and keeps one tile); -1 = no tile
+    auto two_tile = [&](int k) -> int { return k == 0 ? wave : (wave > 0 ? NW + wave - 1 : -1); };
+
     // Partial SRE of this block's candidate tiles t = ju + PU * i, i = ibase + wave +
     // NW * k (k < G): sre_load fetches the phi rows (hi, lo) and the values of a
     // wave's G tiles, sre_math computes them two at a time and publishes the
@@ -281,7 +286,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 #pragma unroll
             for (int q = 0; q < P; ++q) {
                 const int k = k0 + q < G ? k0 + q : G - 1;
-                const int t = ju + PU * (ibase + wave + (k0 + q) * NW);
+                const int it = G == 2 ? two_tile(k0 + q) : ibase + wave + (k0 + q) * NW;
+                const int t = it >= 0 ? ju + PU * it : T;
                 // rows 4qg .. 4qg+2 of dac hold the three parts of d for candidate r16
                 const float dd = (dac[q][0] + dac[q][1]) + dac[q][2];
                 const float inv = dd > 0.f ? __builtin_amdgcn_rcpf(dd) : 0.f;
@@ -318,12 +324,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     int pfcode[2] = {INT_MIN, INT_MIN};
     auto tiles_of_block = [&](int nUq) { const int T = (nUq + 15) / 16; return T > ju ? (T - ju + PU - 1) / PU : 0; };
     auto prefetch_next = [&](int nUq, int cntq, int xq) {
-        const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW;
+        const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW - 1;
         const int T = (nUq + 15) / 16;
         int code[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {  // a tile slot past the last tile holds the code-0 row
-            const int t = ju + PU * (wave + k * NW);
+            const int it = two_tile(k), t = it >= 0 ? ju + PU * it : T;
             int u = t * 16 + r16;
             u = u < nUq ? u : nUq - 1;
             code[k] = use && t < T ? cand_code(u, cntq, xq) : 0;
@@ -340,6 +346,29 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 pfv[k] = *(const uint2*)(code_v(code[k]) + col0 + qg * 4);
                 pfcode[k] = code[k];
             }
+    };
+    // the same for the rows of leaving keys only, whose codes are known before the
+    // selection (waves 1.. load them while wave 0 selects)
+    auto prefetch_new = [&](int nUq, int cntq, int xq) {
+        const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW - 1;
+        const int T = (nUq + 15) / 16;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int it = two_tile(k), t = it >= 0 ? ju + PU * it : T;
+            int u = t * 16 + r16;
+            u = u < nUq ? u : nUq - 1;
+            const int code = xq + (u - cntq);
+            if (use && t < T && u >= cntq && code != pfcode[k]) {
+                const uint16_t* p = code_phs(code) + qg * 8;
+#pragma unroll
+                for (int m = 0; m < FM; ++m) {
+                    pfh[k][m] = *(const uint4*)(p + m * 32);
+                    pfl[k][m] = *(const uint4*)(p + F + m * 32);
+                }
+                pfv[k] = *(const uint2*)(code_v(code) + col0 + qg * 4);
+                pfcode[k] = code;
+            }
+        }
     };
     {
         const Iv v0 = interval(0);
@@ -390,7 +419,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 bf16x8 Ah[FM], Al[FM], As[FM];
                 load_A(Ah, Al, As);
                 const int TB = tiles_of_block(nU);
-                if (TB <= 2 * NW)  // operands loaded during the previous fold (or before the loop)
+                if (TB <= 2 * NW - 1)  // operands loaded during the previous fold (or before the loop)
                     sre_math(Two{}, nU, 0, xw, tag, Ah, Al, As, pfh, pfl, pfv);
                 else
                     for (int ib = 0; ib < TB; ib += RES) {
@@ -606,7 +635,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             else if (nch <= 5) select_compact(std::integral_constant<int, 5>{});
             else if (nch <= 10) select_compact(std::integral_constant<int, 10>{});
             else select_compact(std::integral_constant<int, NCH>{});
-        }
+        } else
+            prefetch_new(nUN, cntN, ivN.xE0);
         lds_sync();
         const int nF = misc[5];
 
