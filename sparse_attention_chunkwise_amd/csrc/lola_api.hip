@@ -114,31 +114,35 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     const Dims& d = a.d;
     const int chains = a.B * d.Hkv;
     if (mark(ev, 0, s) != hipSuccess) return LOLA_ERR_HIP;
-    dim3 gp((a.wl.X + d.C + 63) / 64, chains);
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((prologue_bf16_kernel<D, F / 2>), gp, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
-    if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
-    bool split = false;
+    // the scan variant decides which phi rows the prologue writes: the split scan
+    // (bf16 io) reads the bf16 hi/lo rows only
+    int pu = 0;
+    size_t split_lds = 0;
     if constexpr (sizeof(T) == 2) {
-        const size_t lds = split_smem(F, d.C, d.L).total;
+        split_lds = split_smem(F, d.C, d.L).total;
         // as many candidate groups per column slice (4, 2, then 1) as the device holds at once
-        int pu = 0;
         if (split_allowed())
             for (int g : {4, 2, 1})
-                if (split_fits(scan_split_kernel<D, F>, split_blocks(D, chains, g), lds)) {
+                if (split_fits(scan_split_kernel<D, F>, split_blocks(D, chains, g), split_lds)) {
                     pu = g;
                     break;
                 }
-        if (pu > 0) {
-            if (allow_lds(scan_split_kernel<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
+    }
+    const bool split = pu > 0;
+    dim3 gp((a.wl.X + d.C + 63) / 64, chains);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((prologue_bf16_kernel<D, F / 2>), gp, dim3(256), 0, s, a, split ? 0 : 1);
+    else
+        hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
+    if constexpr (sizeof(T) == 2) {
+        if (split) {
+            if (allow_lds(scan_split_kernel<D, F>, split_lds) != hipSuccess) return LOLA_ERR_HIP;
             void* params[] = {&a};
             if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(scan_split_kernel<D, F>),
                                            dim3(split_blocks(D, chains, pu)), dim3(kSplitThreads), params,
-                                           (unsigned)lds, s) != hipSuccess)
+                                           (unsigned)split_lds, s) != hipSuccess)
                 return LOLA_ERR_HIP;
-            split = true;
         }
     }
     if (!split) {

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
 // row r16 and the two softmaxes combine the four lanes of a row by shuffles.
 // grid (ceil((X + C) / 64), B*Hkv), block 256.
 template <int D, int Fh>
-__global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a)
+__global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_rows)
 {
     constexpr int F = 2 * Fh, FTH = Fh / 16, DS = D / 32;
     const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
@@ -319,11 +319,13 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a)
             ph[ft][i] = valid ? ep[ft][i] / sp : 0.f;
             ph[FTH + ft][i] = valid ? en[ft][i] / sn : 0.f;
         }
-    float* po = row < X ? ws_phiX(a, chain, row) : ws_cphi(a, chain, row - X);
     uint16_t* ps = row < X ? ws_phiS(a, chain, row) : ws_cphiS(a, chain, row - X);
+    if (fp32_rows) {  // fp32 rows: only the one-workgroup scan reads them
+        float* po = row < X ? ws_phiX(a, chain, row) : ws_cphi(a, chain, row - X);
 #pragma unroll
-    for (int T = 0; T < 2 * FTH; ++T)
-        *(float4*)(po + T * 16 + qg * 4) = make_float4(ph[T][0], ph[T][1], ph[T][2], ph[T][3]);
+        for (int T = 0; T < 2 * FTH; ++T)
+            *(float4*)(po + T * 16 + qg * 4) = make_float4(ph[T][0], ph[T][1], ph[T][2], ph[T][3]);
+    }
     // hi / lo parts in operand order: tiles 2m and 2m+1 fill positions m*32 + qg*8 + 0..7
 #pragma unroll
     for (int m = 0; m < FTH; ++m) {
