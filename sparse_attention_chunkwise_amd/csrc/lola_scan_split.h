@@ -766,7 +766,41 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         cnt = cntN;
     }
 
-    // ---- state out: this block's rows of H^T; block 0 also s, cache and window ----
+    // ---- state out ----
+    // Cache rows replaced in this call and the window ring, in 16-byte pieces spread
+    // over the chain's blocks (no block of the scan reads them from the state: the
+    // call-start rows are read from the workspace copies).
+    {
+        constexpr int NP = D / 8;  // pieces per row
+        const int nb = KW * PU, rank = jw + KW * ju;
+        const int nrc = cnt > rank ? (cnt - rank + nb - 1) / nb : 0;  // this block's cache rows
+        for (int q = tid; q < nrc * NP; q += NT) {
+            const int i = rank + nb * (q / NP), pc = (q % NP) * 8, code = cref[i];
+            if (code >= 0) {
+                const uint4 k4 = *(const uint4*)(xrow_k<bf16>(a, chain, b, g, code) + pc);
+                const uint4 v4 = *(const uint4*)(xrow_v<bf16>(a, chain, b, g, code) + pc);
+                *(uint4*)(ch.cache_k<bf16>() + (size_t)i * D + pc) = k4;
+                *(uint4*)(ch.cache_v<bf16>() + (size_t)i * D + pc) = v4;
+            }
+        }
+        if (w > 0) {
+            const int64_t tend = t0 + n;
+            const int64_t p0 = tend - w > t0 ? tend - w : t0;
+            const int nr = (int)(tend - p0);
+            const int nrr = nr > rank ? (nr - rank + nb - 1) / nb : 0;
+            for (int q = tid; q < nrr * NP; q += NT) {
+                const int i = rank + nb * (q / NP), pc = (q % NP) * 8;
+                const int64_t p = p0 + i;
+                const int slot = (int)(p % w);
+                const size_t src = (((size_t)b * n + (size_t)(p - t0)) * d.Hkv + g) * D + pc;
+                const uint4 k4 = *(const uint4*)((const bf16*)a.k + src);
+                const uint4 v4 = *(const uint4*)((const bf16*)a.v + src);
+                *(uint4*)(ch.ring_k<bf16>() + (size_t)slot * D + pc) = k4;
+                *(uint4*)(ch.ring_v<bf16>() + (size_t)slot * D + pc) = v4;
+            }
+        }
+    }
+    // this column slice's rows of H^T (lead blocks); block 0 also s, positions, counts
     if (!lead) return;
 #pragma unroll
     for (int h = 0; h < HT; ++h) {
@@ -790,26 +824,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     lds_sync();
     for (int i = tid; i < F; i += NT) ch.s()[i] = sP[perm_pos(i)];
     for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
-    for (int idx = tid; idx < cnt * D; idx += NT) {
-        const int i = idx / D, j = idx % D;
-        if (cref[i] >= 0) {
-            ch.cache_k<bf16>()[(size_t)i * D + j] = xrow_k<bf16>(a, chain, b, g, cref[i])[j];
-            ch.cache_v<bf16>()[(size_t)i * D + j] = xrow_v<bf16>(a, chain, b, g, cref[i])[j];
-        }
-    }
-    if (w > 0) {
-        const int64_t tend = t0 + n;
-        const int64_t p0 = tend - w > t0 ? tend - w : t0;
-        const int nr = (int)(tend - p0);
-        for (int idx = tid; idx < nr * D; idx += NT) {
-            const int i = idx / D, j = idx % D;
-            const int64_t p = p0 + i;
-            const int slot = (int)(p % w);
-            const size_t src = (((size_t)b * n + (size_t)(p - t0)) * d.Hkv + g) * D + j;
-            ch.ring_k<bf16>()[(size_t)slot * D + j] = ((const bf16*)a.k)[src];
-            ch.ring_v<bf16>()[(size_t)slot * D + j] = ((const bf16*)a.v)[src];
-        }
-    }
     if (tid == 0) {
         ch.cnt() = cnt;
         ch.tok() = t0 + n;
