@@ -904,24 +904,29 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
             make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
     for (int i = tid; i < F; i += NT) ch.s()[i] = sP[perm_pos(i)];
     for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
-    for (int idx = tid; idx < cnt * D; idx += NT) {
-        const int i = idx / D, j = idx % D;
-        if (cref[i] >= 0) {
-            ch.cache_k<T>()[(size_t)i * D + j] = xrow_k<T>(a, chain, b, g, cref[i])[j];
-            ch.cache_v<T>()[(size_t)i * D + j] = xrow_v<T>(a, chain, b, g, cref[i])[j];
+    // cache and window rows in 16-byte pieces
+    constexpr int EP = 16 / (int)sizeof(T), NP = D / EP;
+    static_assert(D % EP == 0, "rows are whole 16-byte pieces");
+    for (int q = tid; q < cnt * NP; q += NT) {
+        const int i = q / NP, pc = (q % NP) * EP, code = cref[i];
+        if (code >= 0) {
+            const uint4 k4 = *(const uint4*)(xrow_k<T>(a, chain, b, g, code) + pc);
+            const uint4 v4 = *(const uint4*)(xrow_v<T>(a, chain, b, g, code) + pc);
+            *(uint4*)(ch.cache_k<T>() + (size_t)i * D + pc) = k4;
+            *(uint4*)(ch.cache_v<T>() + (size_t)i * D + pc) = v4;
         }
     }
     if (w > 0) {
         const int64_t tend = t0 + n;
         const int64_t p0 = tend - w > t0 ? tend - w : t0;
         const int nr = (int)(tend - p0);
-        for (int idx = tid; idx < nr * D; idx += NT) {
-            const int i = idx / D, j = idx % D;
+        for (int q = tid; q < nr * NP; q += NT) {
+            const int i = q / NP, pc = (q % NP) * EP;
             const int64_t p = p0 + i;
             const int slot = (int)(p % w);
-            const size_t src = (((size_t)b * n + (size_t)(p - t0)) * d.Hkv + g) * D + j;
-            ch.ring_k<T>()[(size_t)slot * D + j] = ((const T*)a.k)[src];
-            ch.ring_v<T>()[(size_t)slot * D + j] = ((const T*)a.v)[src];
+            const size_t src = (((size_t)b * n + (size_t)(p - t0)) * d.Hkv + g) * D + pc;
+            *(uint4*)(ch.ring_k<T>() + (size_t)slot * D + pc) = *(const uint4*)((const T*)a.k + src);
+            *(uint4*)(ch.ring_v<T>() + (size_t)slot * D + pc) = *(const uint4*)((const T*)a.v + src);
         }
     }
     if (tid == 0) {
