@@ -119,7 +119,7 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     int pu = 0;
     size_t split_lds = 0;
     if constexpr (sizeof(T) == 2) {
-        split_lds = split_smem(F, d.C, d.L).total;
+        split_lds = split_smem<F>().total;
         // as many candidate groups per column slice (4, 2, then 1) as the device holds at once
         if (split_allowed())
             for (int g : {4, 2, 1})

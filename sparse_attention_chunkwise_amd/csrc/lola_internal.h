@@ -21,7 +21,7 @@ constexpr int kMaxCand = kMaxCache + kMaxChunk;  // |cache| + |leaving keys| per
 constexpr uint32_t kMagic = 0x414c4f4cu;         // "LOLA"
 constexpr uint32_t kVersion = 1;
 
-inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Dims {
     int Hq, Hkv, D, Fh, F, w, C, L, G;

@@ -47,22 +47,25 @@ struct SplitSmem {
     size_t PR, VS, AX, s, sparts, ebits, foldc, cref, cpos, freed, tiep, misc, total;
 };
 
-__host__ __device__ inline SplitSmem split_smem(int F, int C, int L)
+// Every array is sized for the largest cache and chunk, so that all offsets are
+// compile-time constants (immediate LDS offsets, no base registers).
+template <int F>
+__host__ __device__ constexpr SplitSmem split_smem()
 {
-    SplitSmem m;
-    const int U = C + L, Cp = C > 0 ? C : 1, EP = kFoldChunk + 8;
+    SplitSmem m{};
+    constexpr int EP = kFoldChunk + 8;
     size_t off = 0;
     m.PR = off;     off += align_up(sizeof(uint16_t) * 2 * (size_t)F * EP, 16);        // [2F][EP]
     m.VS = off;     off += align_up(sizeof(uint16_t) * 16 * (size_t)EP, 16);          // [16][EP]
     m.AX = off;     off += align_up(sizeof(uint16_t) * 2 * 16 * (size_t)(F + 8), 16); // [2][16][F+8]
     m.s = off;      off += align_up(sizeof(float) * F, 16);
     m.sparts = off; off += align_up(sizeof(uint16_t) * 3 * (size_t)F, 16);            // [3][F]
-    m.ebits = off;  off += sizeof(uint32_t) * U;
-    m.foldc = off;  off += sizeof(int) * U;
-    m.cref = off;   off += sizeof(int) * Cp;
-    m.cpos = off;   off += sizeof(int) * Cp;
-    m.freed = off;  off += sizeof(int) * Cp;
-    m.tiep = off;   off += sizeof(int) * U;
+    m.ebits = off;  off += sizeof(uint32_t) * kMaxCand;
+    m.foldc = off;  off += sizeof(int) * kMaxCand;
+    m.cref = off;   off += sizeof(int) * kMaxCache;
+    m.cpos = off;   off += sizeof(int) * kMaxCache;
+    m.freed = off;  off += sizeof(int) * kMaxCache;
+    m.tiep = off;   off += sizeof(int) * kMaxCand;
     m.misc = off;   off += sizeof(int) * 16;
     m.total = align_up(off, 16);
     return m;
@@ -94,13 +97,14 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
     const int chains = a.B * d.Hkv;
-    const int PU = (int)gridDim.x / (8 * KW * ((chains + 7) / 8));  // candidate groups
+    const int PU = (int)gridDim.x / (8 * KW * ((chains + 7) / 8));  // candidate groups: 1, 2 or 4
+    const int pl = __builtin_ctz((unsigned)PU);                      // log2 PU (shifts, not divisions)
     const int bid = blockIdx.x, xcd = bid & 7, sb = bid >> 3;
-    const int jw = sb % KW, ju = (sb / KW) % PU, chain = (sb / (KW * PU)) * 8 + xcd;
+    const int jw = sb % KW, ju = (sb / KW) & (PU - 1), chain = ((sb / KW) >> pl) * 8 + xcd;
     const bool lead = ju == 0;  // writes this column slice's rows of the snapshots and of H
     if (chain >= chains) return;  // the whole chain is absent: none of its blocks waits
     const int col0 = 16 * jw;
-    const SplitSmem sm = split_smem(F, C, L);
+    constexpr SplitSmem sm = split_smem<F>();
     uint16_t* PR = (uint16_t*)(smem + sm.PR);      // folded pairs transposed: row = phi hi | lo slot, column = pair
     uint16_t* VS = (uint16_t*)(smem + sm.VS);      // folded pairs' values, this block's 16 columns, transposed
     uint16_t* AX = (uint16_t*)(smem + sm.AX);      // hi, lo of H^T rows col0.. (operand order)
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     uint4 pfh[2][FM], pfl[2][FM];
     uint2 pfv[2];
     int pfcode[2] = {INT_MIN, INT_MIN};
-    auto tiles_of_block = [&](int nUq) { const int T = (nUq + 15) / 16; return T > ju ? (T - ju + PU - 1) / PU : 0; };
+    auto tiles_of_block = [&](int nUq) { const int T = (nUq + 15) / 16; return T > ju ? (T - ju + PU - 1) >> pl : 0; };
     auto prefetch_next = [&](int nUq, int cntq, int xq) {
         const bool use = nUq > C && C > 0 && tiles_of_block(nUq) <= 2 * NW - 1;
         const int T = (nUq + 15) / 16;
@@ -393,13 +397,13 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                                 (size_t)(col0 + r16) * F + qg * 8;
 #pragma unroll
                 for (int m = 0; m < FM; ++m)
-                    if (m % PU == ju) *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
+                    if ((m & (PU - 1)) == ju) *(uint4*)(dst + m * 32) = *(const uint4*)(AX + r16 * AXS + m * 32 + qg * 8);
             }
-            if (jw == 1 % KW && ju == 1 % PU) {
+            if (jw == 1 % KW && ju == (1 & (PU - 1))) {
                 float* snapS = (float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
                 for (int i = tid; i < F; i += NT) snapS[i] = sP[perm_pos(i)];
             }
-            if (jw == 2 % KW && ju == 2 % PU) {
+            if (jw == 2 % KW && ju == (2 & (PU - 1))) {
                 int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
                 for (int i = tid; i < cnt; i += NT) snapRef[i] = cref[i];
                 if (tid == 0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
@@ -772,8 +776,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     // call-start rows are read from the workspace copies).
     {
         constexpr int NP = D / 8;  // pieces per row
-        const int nb = KW * PU, rank = jw + KW * ju;
-        const int nrc = cnt > rank ? (cnt - rank + nb - 1) / nb : 0;  // this block's cache rows
+        const int nb = KW * PU, nbl = __builtin_ctz((unsigned)KW) + pl, rank = jw + KW * ju;
+        const int nrc = cnt > rank ? (cnt - rank + nb - 1) >> nbl : 0;  // this block's cache rows
         for (int q = tid; q < nrc * NP; q += NT) {
             const int i = rank + nb * (q / NP), pc = (q % NP) * 8, code = cref[i];
             if (code >= 0) {
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             const int64_t tend = t0 + n;
             const int64_t p0 = tend - w > t0 ? tend - w : t0;
             const int nr = (int)(tend - p0);
-            const int nrr = nr > rank ? (nr - rank + nb - 1) / nb : 0;
+            const int nrr = nr > rank ? (nr - rank + nb - 1) >> nbl : 0;
             for (int q = tid; q < nrr * NP; q += NT) {
                 const int i = rank + nb * (q / NP), pc = (q % NP) * 8;
                 const int64_t p = p0 + i;
