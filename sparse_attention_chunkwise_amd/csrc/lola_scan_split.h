@@ -40,7 +40,6 @@ namespace lola {
 
 constexpr int kSplitThreads = 256;                    // 4 waves, one per SIMD
 constexpr int kSplitGroup = 5;                        // candidate tiles per wave per load round
-constexpr int kSelChunks = (kMaxCand + 63) / 64;      // 64-candidate chunks a wave holds for selection
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 struct SplitSmem {
@@ -90,7 +89,7 @@ template <int D, int F>
 __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 {
     constexpr int KW = D / 16, NT = kSplitThreads, NW = NT / 64, FT = F / 16, FM = F / 32;
-    constexpr int EC = kFoldChunk, EP = EC + 8, AXS = F + 8, GR = kSplitGroup, NCH = kSelChunks;
+    constexpr int EC = kFoldChunk, EP = EC + 8, AXS = F + 8, GR = kSplitGroup;
     constexpr int RES = NW * GR, HT = (FT + NW - 1) / NW;
     static_assert(EC * 4 == NT && EC == 64 && (2 * F / 8) % (2 * NW) == 0, "fold staging covers the chunk exactly");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -634,11 +633,124 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 }
                 if (lane == 0) misc[5] = nF;
             };
+            // The same selection for more than 5 chunks, with runtime loops over the
+            // chunks and the keys read from LDS at each use: no per-chunk registers, so
+            // the wide case does not raise the register pressure of the whole kernel.
+            auto select_wide = [&]() {
+                const int nch = (nU + 63) / 64;
+                auto key_at = [&](int u) -> uint32_t { return u < nU ? ebits[u] : 0u; };
+                uint32_t tau = 0u;
+                bool split_ties = false;
+                int need = 0, nt = 0;
+                if (needSel) {
+                    uint32_t lo = 0u, hi = 0x80000000u;
+                    int clo = nU, chi = 0;
+                    auto probe = [&](uint32_t t) -> int {
+                        int cc = 0;
+#pragma unroll 4
+                        for (int i = 0; i < nch; ++i) cc += __popcll(__ballot(key_at(i * 64 + lane) >= t));
+                        cc = __builtin_amdgcn_readfirstlane(cc);
+                        if (cc >= C) {
+                            lo = t;
+                            clo = cc;
+                        } else {
+                            hi = t;
+                            chi = cc;
+                        }
+                        return cc;
+                    };
+                    int cc = probe(tauPrev > 0u && tauPrev < hi ? tauPrev : 0x3f800000u);
+                    uint32_t step = 1u << 18;
+#pragma nounroll
+                    while (cc != C && hi - lo > 2u * step) {
+                        cc = probe(cc >= C ? lo + step : hi - step);
+                        step = step < (1u << 28) ? step << 2 : step;
+                    }
+                    uint32_t wprev = 0xffffffffu;
+                    int k = 0;
+#pragma nounroll
+                    while (cc != C && hi - lo > 1u) {
+                        const uint32_t wd = hi - lo;
+                        uint32_t t;
+                        if ((k & 1) && wd > wprev / 2u)
+                            t = lo + wd / 2u;
+                        else {
+                            const float frac = ((float)(clo - C) + 0.5f) * __builtin_amdgcn_rcpf((float)(clo - chi));
+                            t = lo + (uint32_t)((float)wd * frac);
+                            t = t <= lo ? lo + 1u : (t >= hi ? hi - 1u : t);
+                            t = __builtin_amdgcn_readfirstlane(t);
+                        }
+                        if (!(k & 1)) wprev = wd;
+                        ++k;
+                        cc = probe(t);
+                    }
+                    tau = lo;
+                    tauPrev = lo;
+                    if (clo != C) {
+                        int above = 0, ties = 0;
+                        for (int i = 0; i < nch; ++i) {
+                            const int u = i * 64 + lane;
+                            const uint32_t kv = key_at(u);
+                            above += __popcll(__ballot(u < nU && kv > tau));
+                            ties += __popcll(__ballot(u < nU && kv == tau));
+                        }
+                        need = C - above;
+                        split_ties = ties > need;
+                        if (split_ties) {
+                            for (int i = 0; i < nch; ++i) {
+                                const int u = i * 64 + lane;
+                                const bool tie = u < nU && key_at(u) == tau;
+                                const uint64_t bm = __ballot(tie);
+                                if (tie) tiep[nt + __popcll(bm & lt)] = cand_pos(u);
+                                nt += __popcll(bm);
+                            }
+                            lds_wait();
+                        }
+                    }
+                }
+                // kept: above the threshold, or tied and among the `need` oldest tied positions
+                auto kept = [&](int u) -> bool {
+                    if (u >= nU) return false;
+                    if (!needSel) return nU <= C;
+                    const uint32_t kv = ebits[u];
+                    if (kv != tau) return kv > tau;
+                    if (!split_ties) return true;
+                    const int p = cand_pos(u);
+                    int rank = 0;
+                    for (int j = 0; j < nt; ++j) rank += tiep[j] < p;
+                    return rank < need;
+                };
+                int nF = 0, nFr = 0;
+                for (int i = 0; i < nch; ++i) {
+                    const int u = i * 64 + lane;
+                    const bool isF = u < nU && !kept(u);
+                    const bool isFr = isF && u < cnt;
+                    const uint64_t bF = __ballot(isF), bFr = __ballot(isFr);
+                    if (isF) foldc[nF + __popcll(bF & lt)] = cand_code(u, cnt, xE0);
+                    if (isFr) freed[nFr + __popcll(bFr & lt)] = u;
+                    nF += __popcll(bF);
+                    nFr += __popcll(bFr);
+                }
+                lds_wait();
+                int nK = 0;
+                for (int i = cnt / 64; i < nch; ++i) {
+                    const int u = i * 64 + lane;
+                    const bool isK = u >= cnt && kept(u);
+                    const uint64_t bK = __ballot(isK);
+                    if (isK) {
+                        const int ki = nK + __popcll(bK & lt);
+                        const int slot = ki < nFr ? freed[ki] : cnt + (ki - nFr);
+                        cref[slot] = xE0 + (u - cnt);
+                        cpos[slot] = (int)(eS + (u - cnt));
+                    }
+                    nK += __popcll(bK);
+                }
+                if (lane == 0) misc[5] = nF;
+            };
             const int nch = (nU + 63) / 64;
             if (nch <= 2) select_compact(std::integral_constant<int, 2>{});
             else if (nch <= 5) select_compact(std::integral_constant<int, 5>{});
-            else if (nch <= 10) select_compact(std::integral_constant<int, 10>{});
-            else select_compact(std::integral_constant<int, NCH>{});
+            else select_wide();
         } else
             prefetch_new(nUN, cntN, ivN.xE0);
         lds_sync();
