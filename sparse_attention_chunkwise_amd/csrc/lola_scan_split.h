@@ -493,6 +493,34 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int cntN = nU < C ? nU : C;
         const Iv ivN = interval(c + 1 < NI ? c + 1 : c);
         const int nUN = c + 1 < NI ? cntN + ivN.nE : 0;
+        uint32_t kbits = 0u;  // wave 0: bit i set = the lane's candidate of chunk i stays
+        // Slot update (wave 0, while the fold rows load): folded cache pairs free their
+        // slots in slot order, and the kept leaving keys take the freed slots in order,
+        // then new slots past the count.
+        auto slot_update = [&]() {
+            int nFr = 0;
+            for (int i = 0; i < (cnt + 63) / 64; ++i) {
+                const int u = i * 64 + lane;
+                const bool isFr = u < cnt && !((kbits >> i) & 1u);
+                const uint64_t b = __ballot(isFr);
+                if (isFr) freed[nFr + __popcll(b & lt)] = u;
+                nFr += __popcll(b);
+            }
+            lds_wait();
+            int nK = 0;
+            for (int i = cnt / 64; i < (nU + 63) / 64; ++i) {
+                const int u = i * 64 + lane;
+                const bool isK = u >= cnt && u < nU && ((kbits >> i) & 1u);
+                const uint64_t bK = __ballot(isK);
+                if (isK) {
+                    const int ki = nK + __popcll(bK & lt);
+                    const int slot = ki < nFr ? freed[ki] : cnt + (ki - nFr);
+                    cref[slot] = xE0 + (u - cnt);
+                    cpos[slot] = (int)(eS + (u - cnt));
+                }
+                nK += __popcll(bK);
+            }
+        };
         if (wave == 0) {
             auto cand_pos = [&](int u) -> int { return u < cnt ? cpos[u] : (int)(eS + (u - cnt)); };
             // NC = candidate chunks of 64 held per lane (a compile-time bound >= ceil(nU / 64))
@@ -602,35 +630,19 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                         }
                     }
                 }
-                // compaction in candidate order: fold list, freed cache slots, then the
-                // kept leaving keys take the freed slots in order, then new slots
-                int nF = 0, nFr = 0;
+                // fold list in candidate order; the keep bits go to the slot update
+                int nF = 0;
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
-                    const int u = i * 64 + lane;
                     const bool isF = ((vm[i] & ~km[i]) >> lane) & 1ull;
-                    const bool isFr = isF && u < cnt;
-                    const uint64_t bF = __ballot(isF), bFr = __ballot(isFr);
+                    const uint64_t bF = __ballot(isF);
                     if (isF) foldc[nF + __popcll(bF & lt)] = ucv[i];
-                    if (isFr) freed[nFr + __popcll(bFr & lt)] = u;
                     nF += __popcll(bF);
-                    nFr += __popcll(bFr);
                 }
-                lds_wait();
-                int nK = 0;
+                uint32_t kb = 0u;
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    const int u = i * 64 + lane;
-                    const bool isK = ((km[i] >> lane) & 1ull) && u >= cnt;
-                    const uint64_t bK = __ballot(isK);
-                    if (isK) {
-                        const int ki = nK + __popcll(bK & lt);
-                        const int slot = ki < nFr ? freed[ki] : cnt + (ki - nFr);
-                        cref[slot] = xE0 + (u - cnt);
-                        cpos[slot] = (int)(eS + (u - cnt));
-                    }
-                    nK += __popcll(bK);
-                }
+                for (int i = 0; i < NC; ++i) kb |= (uint32_t)((km[i] >> lane) & 1ull) << i;
+                kbits = kb;
                 if (lane == 0) misc[5] = nF;
             };
             // The same selection for more than 5 chunks, with runtime loops over the
@@ -720,31 +732,18 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     for (int j = 0; j < nt; ++j) rank += tiep[j] < p;
                     return rank < need;
                 };
-                int nF = 0, nFr = 0;
+                int nF = 0;
+                uint32_t kb = 0u;
                 for (int i = 0; i < nch; ++i) {
                     const int u = i * 64 + lane;
-                    const bool isF = u < nU && !kept(u);
-                    const bool isFr = isF && u < cnt;
-                    const uint64_t bF = __ballot(isF), bFr = __ballot(isFr);
+                    const bool keep = kept(u);
+                    const bool isF = u < nU && !keep;
+                    const uint64_t bF = __ballot(isF);
                     if (isF) foldc[nF + __popcll(bF & lt)] = cand_code(u, cnt, xE0);
-                    if (isFr) freed[nFr + __popcll(bFr & lt)] = u;
                     nF += __popcll(bF);
-                    nFr += __popcll(bFr);
+                    kb |= (uint32_t)keep << i;
                 }
-                lds_wait();
-                int nK = 0;
-                for (int i = cnt / 64; i < nch; ++i) {
-                    const int u = i * 64 + lane;
-                    const bool isK = u >= cnt && kept(u);
-                    const uint64_t bK = __ballot(isK);
-                    if (isK) {
-                        const int ki = nK + __popcll(bK & lt);
-                        const int slot = ki < nFr ? freed[ki] : cnt + (ki - nFr);
-                        cref[slot] = xE0 + (u - cnt);
-                        cpos[slot] = (int)(eS + (u - cnt));
-                    }
-                    nK += __popcll(bK);
-                }
+                kbits = kb;
                 if (lane == 0) misc[5] = nF;
             };
             const int nch = (nU + 63) / 64;
@@ -763,11 +762,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int ve1 = tid >> 2, vq4 = (tid & 3) * 4;  // EC * 4 == NT value pieces
         uint4 t4[SPT];
         uint2 t2;
+        uint32_t k0 = 0u, k1 = 0u, vkeep = 0u;  // keep masks of the staged rows
         // Lane l of wave w stages pairs 2 (l % 32) and 2 (l % 32) + 1, 16-byte column
         // groups cg = 2 w + l / 32 + 2 NW m, and writes them transposed (one dword =
         // one slot of the two pairs, consecutive lanes on consecutive dwords).  Rows
         // past the chunk end load the chunk's last pair and are zeroed after the
-        // load, so that every lookup and load is issued without a branch.
+        // store, so that every lookup and load is issued without a branch.
         constexpr int CG = SPT / 2;  // column groups per lane
         const int rp = lane & 31, cg0 = 2 * wave + (lane >> 5);
         auto stage_load = [&](int e0) {
@@ -775,32 +775,27 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             const int c0 = foldc[e0 + (2 * rp < ne ? 2 * rp : ne - 1)];
             const int c1 = foldc[e0 + (2 * rp + 1 < ne ? 2 * rp + 1 : ne - 1)];
             const int vcode = foldc[e0 + (ve1 < ne ? ve1 : ne - 1)];
-            const uint2 y = *(const uint2*)(code_v(vcode) + col0 + vq4);
+            t2 = *(const uint2*)(code_v(vcode) + col0 + vq4);
             const uint16_t* p0 = code_phs(c0);
             const uint16_t* p1 = code_phs(c1);
-            uint4 x[SPT];
 #pragma unroll
             for (int m = 0; m < CG; ++m) {
                 const int c8 = (cg0 + 2 * NW * m) * 8;
-                x[2 * m] = *(const uint4*)(p0 + c8);
-                x[2 * m + 1] = *(const uint4*)(p1 + c8);
+                t4[2 * m] = *(const uint4*)(p0 + c8);
+                t4[2 * m + 1] = *(const uint4*)(p1 + c8);
             }
-            const uint32_t k0 = 2 * rp < ne ? 0xffffffffu : 0u, k1 = 2 * rp + 1 < ne ? 0xffffffffu : 0u;
-#pragma unroll
-            for (int m = 0; m < CG; ++m) {
-                t4[2 * m] = make_uint4(x[2 * m].x & k0, x[2 * m].y & k0, x[2 * m].z & k0, x[2 * m].w & k0);
-                t4[2 * m + 1] = make_uint4(x[2 * m + 1].x & k1, x[2 * m + 1].y & k1, x[2 * m + 1].z & k1,
-                                           x[2 * m + 1].w & k1);
-            }
-            const uint32_t vkeep = ve1 < ne ? 0xffffffffu : 0u;
-            t2 = make_uint2(y.x & vkeep, y.y & vkeep);
+            k0 = 2 * rp < ne ? 0xffffffffu : 0u;
+            k1 = 2 * rp + 1 < ne ? 0xffffffffu : 0u;
+            vkeep = ve1 < ne ? 0xffffffffu : 0u;
         };
+        // (the masks are applied here, so that stage_load returns with its loads in flight)
         auto stage_store = [&]() {
 #pragma unroll
             for (int m = 0; m < CG; ++m) {
                 const int c8 = (cg0 + 2 * NW * m) * 8;
-                const uint32_t a4[4] = {t4[2 * m].x, t4[2 * m].y, t4[2 * m].z, t4[2 * m].w};
-                const uint32_t b4[4] = {t4[2 * m + 1].x, t4[2 * m + 1].y, t4[2 * m + 1].z, t4[2 * m + 1].w};
+                const uint32_t a4[4] = {t4[2 * m].x & k0, t4[2 * m].y & k0, t4[2 * m].z & k0, t4[2 * m].w & k0};
+                const uint32_t b4[4] = {t4[2 * m + 1].x & k1, t4[2 * m + 1].y & k1, t4[2 * m + 1].z & k1,
+                                        t4[2 * m + 1].w & k1};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const uint32_t lo = (a4[j >> 1] >> (16 * (j & 1))) & 0xffffu;
@@ -808,10 +803,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     *(uint32_t*)(PR + (c8 + j) * EP + 2 * rp) = lo | (hi << 16);
                 }
             }
-            VS[(vq4 + 0) * EP + ve1] = (uint16_t)(t2.x & 0xffffu);
-            VS[(vq4 + 1) * EP + ve1] = (uint16_t)(t2.x >> 16);
-            VS[(vq4 + 2) * EP + ve1] = (uint16_t)(t2.y & 0xffffu);
-            VS[(vq4 + 3) * EP + ve1] = (uint16_t)(t2.y >> 16);
+            const uint32_t vx = t2.x & vkeep, vy = t2.y & vkeep;
+            VS[(vq4 + 0) * EP + ve1] = (uint16_t)(vx & 0xffffu);
+            VS[(vq4 + 1) * EP + ve1] = (uint16_t)(vx >> 16);
+            VS[(vq4 + 2) * EP + ve1] = (uint16_t)(vy & 0xffffu);
+            VS[(vq4 + 3) * EP + ve1] = (uint16_t)(vy >> 16);
         };
         auto fold_mma = [&]() {
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80,
@@ -837,17 +833,14 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     for (int i = 0; i < 4; ++i) sP[perm_pos(ft * 16 + qg * 4 + i)] += sa[i];
             }
         };
-        if (nF > 0) {
-            stage_load(0);
-            stage_store();
-        }
+        if (nF > 0) stage_load(0);
+        if (wave == 0) slot_update();
+        if (nF > 0) stage_store();
+        lds_sync();  // first chunk staged, slot codes updated
         // the next interval's SRE operands, issued once the first chunk is staged (so
         // that they do not queue ahead of its loads); they arrive during the fold
         prefetch_next(nUN, cntN, ivN.xE0);
-        if (nF > 0) {
-            lds_sync();
-            fold_mma();
-        }
+        if (nF > 0) fold_mma();
         for (int e0 = EC; e0 < nF; e0 += EC) {
             lds_sync();  // the previous chunk is consumed
             stage_load(e0);
