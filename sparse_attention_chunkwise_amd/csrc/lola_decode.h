@@ -224,10 +224,8 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
         for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        zmax = quad_max(zmax);
+        zmin = quad_min(zmin);
         float hk[NH];
         float sp = 0.f, sn = 0.f;
 #pragma unroll
@@ -240,17 +238,14 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
                 sp += e1;
                 sn += e2;
             }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
+        sp = quad_sum(sp);
+        sn = quad_sum(sn);
 #pragma unroll
         for (int j = 0; j < NH / 2; ++j) { hk[j] /= sp; hk[NH / 2 + j] /= sn; }
         float dd = 0.f;
 #pragma unroll
         for (int j = 0; j < NH; ++j) dd += hk[j] * ss[held_feature<Fh>(qg, j)];
-        dd += __shfl_xor(dd, 16, 64);
-        dd += __shfl_xor(dd, 32, 64);
+        dd = quad_sum(dd);
         // n^T = H^T phi^T ; error over the lane's d rows
         const T* vr = candv(uv ? u : 0);
         float e = 0.f;
@@ -268,8 +263,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
                 e += df * df;
             }
         }
-        e += __shfl_xor(e, 16, 64);
-        e += __shfl_xor(e, 32, 64);
+        e = quad_sum(e);
         if (qg == 0 && uv) esc[u] = e;
     }
     __syncthreads();

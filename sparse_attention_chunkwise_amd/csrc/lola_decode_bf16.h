@@ -100,10 +100,8 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
         for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[p][ft][i]); zmin = fminf(zmin, zt[p][ft][i]); }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        zmax = quad_max(zmax);
+        zmin = quad_min(zmin);
         float sp = 0.f, sn = 0.f;
 #pragma unroll
         for (int ft = 0; ft < Fh / 16; ++ft)
@@ -115,10 +113,8 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
                 sp += e1;
                 sn += e2;
             }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
+        sp = quad_sum(sp);
+        sn = quad_sum(sn);
         const float isp = 1.f / sp, isn = 1.f / sn;
 #pragma unroll
         for (int h = 0; h < F / 4; ++h) x[p][h] *= h < Fh / 4 ? isp : isn;
@@ -254,8 +250,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                     bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
                     bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
                 }
-                dd += __shfl_xor(dd, 16, 64);
-                dd += __shfl_xor(dd, 32, 64);
+                dd = quad_sum(dd);
                 inv[p] = dd > 0.f ? 1.f / dd : 0.f;
             }
         }
@@ -292,8 +287,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            es[p] += __shfl_xor(es[p], 16, 64);
-            es[p] += __shfl_xor(es[p], 32, 64);
+            es[p] = quad_sum(es[p]);
             e[p] = es[p];
         }
     };
@@ -346,10 +340,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        zmax = quad_max(zmax);
+        zmin = quad_min(zmin);
         float hv[F / 4];
         float sp = 0.f, sn = 0.f;
 #pragma unroll
@@ -362,10 +354,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 sp += e1;
                 sn += e2;
             }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
+        sp = quad_sum(sp);
+        sn = quad_sum(sn);
         const float isp = 1.f / sp, isn = 1.f / sn;
         float z = 0.f, kap = 0.f;
 #pragma unroll
@@ -384,10 +374,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             }
             pf[mf] = __builtin_bit_cast(bf16x8, u);
         }
-        z += __shfl_xor(z, 16, 64);
-        z += __shfl_xor(z, 32, 64);
-        kap += __shfl_xor(kap, 16, 64);
-        kap += __shfl_xor(kap, 32, 64);
+        z = quad_sum(z);
+        kap = quad_sum(kap);
         if (!hasE) kap = 0.f;
         zl = z + kap;
         // the leaving key's linear weight per query column, for the linear read of wave 0
@@ -504,8 +492,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 lg[j] = tau * sT[tt][i];
                 if (ok[j]) bmax = fmaxf(bmax, lg[j]);
             }
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+            bmax = quad_max(bmax);
             const float mnew = fmaxf(mrun, bmax);
             const float resc = __expf(mrun - mnew);
             mrun = mnew;
@@ -534,8 +521,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         float* mZ = mrg + NW * 16;       // [NW][16]
         float* mO = mrg + 2 * NW * 16;   // [NW][D][16]
         float Z = Zp;
-        Z += __shfl_xor(Z, 16, 64);
-        Z += __shfl_xor(Z, 32, 64);
+        Z = quad_sum(Z);
         if (qg == 0) { mM[wave * 16 + r16] = mrun; mZ[wave * 16 + r16] = Z; }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)

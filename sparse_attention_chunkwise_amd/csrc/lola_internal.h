@@ -23,6 +23,26 @@ constexpr uint32_t kVersion = 1;
 
 constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Combine the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave: op(x, x^16) first, then
+// op with the same of lane ^ 32, as two __shfl_xor steps would (same operands, same
+// order), but with the lane-swap instructions of gfx950 (VALU, no LDS round trip).
+// Each swap leaves one of the two partners' values in each output register.
+#define LOLA_QUAD_COMBINE(name, OP)                                                             \
+    __device__ __forceinline__ float name(float x)                                              \
+    {                                                                                           \
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), \
+                                                        false, false);                          \
+        x = OP(__uint_as_float(a[0]), __uint_as_float(a[1]));                                   \
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), \
+                                                        false, false);                          \
+        return OP(__uint_as_float(b[0]), __uint_as_float(b[1]));                                \
+    }
+__device__ __forceinline__ float lola_add(float a, float b) { return a + b; }
+LOLA_QUAD_COMBINE(quad_sum, lola_add)
+LOLA_QUAD_COMBINE(quad_max, fmaxf)
+LOLA_QUAD_COMBINE(quad_min, fminf)
+#undef LOLA_QUAD_COMBINE
+
 struct Dims {
     int Hq, Hkv, D, Fh, F, w, C, L, G;
     int io;       // 0 = f32, 1 = bf16

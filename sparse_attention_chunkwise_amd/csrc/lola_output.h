@@ -147,10 +147,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        zmax = quad_max(zmax);
+        zmin = quad_min(zmin);
         float ph[Fh / 4], pn[Fh / 4];
         float sp = 0.f, sn = 0.f;
 #pragma unroll
@@ -162,10 +160,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                 sp += ph[ft * 4 + i];
                 sn += pn[ft * 4 + i];
             }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
+        sp = quad_sum(sp);
+        sn = quad_sum(sn);
         const float isp = 1.f / sp, isn = 1.f / sn;
         // operand order: step mf covers feature tiles 2mf, 2mf+1; features ft*16+qg*4+i
         float hv[F / 4];
@@ -187,8 +183,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             }
             pf[rt][mf] = __builtin_bit_cast(bf16x8, u);
         }
-        z += __shfl_xor(z, 16, 64);
-        z += __shfl_xor(z, 32, 64);
+        z = quad_sum(z);
         zl[rt] = z;
     }
 
@@ -325,8 +320,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                 lg[j] = tau * sT[rt][tt][i];
                 if (kd == 1) bmax = fmaxf(bmax, lg[j]);
             }
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+            bmax = quad_max(bmax);
             const float mnew = fmaxf(mrun[rt], bmax);
             const float resc = __expf(mrun[rt] - mnew);
             mrun[rt] = mnew;
@@ -366,8 +360,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         float Z = Zp[rt];
-        Z += __shfl_xor(Z, 16, 64);
-        Z += __shfl_xor(Z, 32, 64);
+        Z = quad_sum(Z);
         if (qv[rt]) {
             bf16* op = (bf16*)a.out + (((size_t)b * a.n + (size_t)(tq[rt] - t0)) * d.Hq + hq_[rt]) * D;
             const float inv = 1.f / Z;

@@ -291,10 +291,8 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
             zmax = fmaxf(zmax, zt[ft][i]);
             zmin = fminf(zmin, zt[ft][i]);
         }
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-    zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-    zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+    zmax = quad_max(zmax);
+    zmin = quad_min(zmin);
     float ep[FTH][4], en[FTH][4], sp = 0.f, sn = 0.f;
 #pragma unroll
     for (int ft = 0; ft < FTH; ++ft)
@@ -305,10 +303,8 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
             sp += ep[ft][i];
             sn += en[ft][i];
         }
-    sp += __shfl_xor(sp, 16, 64);
-    sp += __shfl_xor(sp, 32, 64);
-    sn += __shfl_xor(sn, 16, 64);
-    sn += __shfl_xor(sn, 32, 64);
+    sp = quad_sum(sp);
+    sn = quad_sum(sn);
     if (row >= X + C) return;
     const bool valid = src != nullptr;
     float ph[2 * FTH][4];  // feature tile T: + half T < FTH, - half T >= FTH
@@ -664,8 +660,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
                         const float df = (acc[t2][i] + acc2[t2][i]) * inv - vv[i];
                         e += df * df;
                     }
-                    e += __shfl_xor(e, 16, 64);
-                    e += __shfl_xor(e, 32, 64);
+                    e = quad_sum(e);
                     if (qg == 0 && u < nU) part[wave * U + u] = e;
                 }
             }
@@ -1033,10 +1028,8 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
                 zmax = fmaxf(zmax, zt[ft][i]);
                 zmin = fminf(zmin, zt[ft][i]);
             }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 16, 64));
-        zmin = fminf(zmin, __shfl_xor(zmin, 32, 64));
+        zmax = quad_max(zmax);
+        zmin = quad_min(zmin);
         float sp = 0.f, sn = 0.f;
 #pragma unroll
         for (int ft = 0; ft < Fh / 16; ++ft)
@@ -1048,10 +1041,8 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
                 sp += ep_;
                 sn += en_;
             }
-        sp += __shfl_xor(sp, 16, 64);
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 16, 64);
-        sn += __shfl_xor(sn, 32, 64);
+        sp = quad_sum(sp);
+        sn = quad_sum(sn);
 #pragma unroll
         for (int j = 0; j < NH / 2; ++j) {
             hq[j] /= sp;
@@ -1081,8 +1072,7 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
     float zl = 0.f;
 #pragma unroll
     for (int j = 0; j < NH; ++j) zl += hq[j] * sS[held_feature<Fh>(qg, j)];
-    zl += __shfl_xor(zl, 16, 64);
-    zl += __shfl_xor(zl, 32, 64);
+    zl = quad_sum(zl);
     float Zp = qg == 0 ? zl : 0.f;  // per-lane partial of the denominator
     float mrun = 0.f;               // running max, floored at 0 (linear terms carry e^-M)
 
@@ -1154,8 +1144,7 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
             lg[j] = tau * sT[tt][i];
             if (kd == 1) bmax = fmaxf(bmax, lg[j]);
         }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        bmax = quad_max(bmax);
         const float mnew = fmaxf(mrun, bmax);
         const float resc = expf(mrun - mnew);
         mrun = mnew;
@@ -1197,8 +1186,7 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
 
     // ---- finish: shared denominator, store o[t][h][d] ----
     float Z = Zp;
-    Z += __shfl_xor(Z, 16, 64);
-    Z += __shfl_xor(Z, 32, 64);
+    Z = quad_sum(Z);
     if (qvalid) {
         T* op = (T*)a.out + (((size_t)b * a.n + (size_t)(t - t0)) * d.Hq + h) * D;
         const float inv = 1.f / Z;

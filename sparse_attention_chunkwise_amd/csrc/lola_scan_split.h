@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     constexpr int EC = kFoldChunk, EP = EC + 8, AXS = F + 8, GR = kSplitGroup;
     constexpr int RES = NW * GR, HT = (FT + NW - 1) / NW;
     static_assert(EC * 4 == NT && EC == 64 && (2 * F / 8) % (2 * NW) == 0, "fold staging covers the chunk exactly");
+    static_assert(5 * 64 <= kMaxCache && 5 * 64 <= kMaxCand, "register selection reads 5 chunks of cref and ebits");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
@@ -302,8 +303,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     const float df = (acc[q][i] + acc2[q][i]) * inv - vv[i];
                     e += df * df;
                 }
-                e += __shfl_xor(e, 16, 64);
-                e += __shfl_xor(e, 32, 64);
+                e = quad_sum(e);
                 const int u = t * 16 + r16;
                 if (qg == 0 && k0 + q < G && t < T && u < nUq)
                     __hip_atomic_store(&xw[u], ((uint64_t)tag << 32) | __float_as_uint(e), __ATOMIC_RELAXED,
@@ -529,11 +529,14 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 uint32_t key[NC];
                 int ucv[NC];              // candidate codes
                 uint64_t km[NC], vm[NC];  // keep and valid masks per chunk
+                // (both arrays hold at least 64 NC entries: the loads need no branch)
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
                     const int u = i * 64 + lane;
-                    key[i] = (needSel && u < nU) ? ebits[u] : 0u;
-                    ucv[i] = u < nU ? cand_code(u, cnt, xE0) : 0;
+                    const uint32_t eb = ebits[u];
+                    const int cr = cref[u];
+                    key[i] = (needSel && u < nU) ? eb : 0u;
+                    ucv[i] = u < cnt ? cr : xE0 + (u - cnt);
                     vm[i] = __ballot(u < nU);
                     km[i] = (!needSel && nU <= C) ? vm[i] : 0ull;
                 }
