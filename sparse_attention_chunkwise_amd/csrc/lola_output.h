@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
             const int idx = tid + k * NT, kr = (idx / (D / 8)) % KB, un = idx % (D / 8);                             \
             const int kidx = (BASE) + kr, kc = kidx < nK ? kidx : 0;                                                 \
-            const bf16* kp = kc < nSpan ? xrow_k<bf16>(a, chain, b, g, xs0 + kc) : ref_k<bf16>(a, chain, b, g, sref[kc - nSpan]); \
+            const int rf = sref[kc >= nSpan ? kc - nSpan : 0];                                                       \
+            const bf16* kp = ref_k<bf16>(a, chain, b, g, kc < nSpan ? xs0 + kc : rf);                                \
             const uint4 k4 = *(const uint4*)(kp + un * 8);                                                           \
             pk[k] = kidx < nK ? k4 : make_uint4(0, 0, 0, 0);                                                         \
         }                                                                                                            \
@@ -232,7 +233,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             const int pr = tid / (D / 8), un = tid % (D / 8);                                                        \
             _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
                 const int kidx = (BASE) + 2 * pr + k, kc = kidx < nK ? kidx : 0;                                     \
-                const bf16* vp = kc < nSpan ? xrow_v<bf16>(a, chain, b, g, xs0 + kc) : ref_v<bf16>(a, chain, b, g, sref[kc - nSpan]); \
+                const int rf = sref[kc >= nSpan ? kc - nSpan : 0];                                                   \
+                const bf16* vp = ref_v<bf16>(a, chain, b, g, kc < nSpan ? xs0 + kc : rf);                            \
                 const uint4 v4 = *(const uint4*)(vp + un * 8);                                                       \
                 pv[k] = kidx < nK ? v4 : make_uint4(0, 0, 0, 0);                                                     \
             }                                                                                                        \
@@ -305,20 +307,16 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             // query position relative to the span start; span key kidx sits at sp0 + kidx
             const int tr = qv[rt] ? (int)(tq[rt] - sp0) : -1;
 #pragma unroll
+            // kind 1: softmax key (in the query's window, or a cache key), 2: linear key
+            // (left the window inside the interval, before the query), 0: masked; all
+            // selects, no branches
             for (int j = 0; j < NJ; ++j) {
                 const int tt = j >> 2, i = j & 3;
                 const int kidx = base + tt * 16 + qg * 4 + i;
-                int kd = 0;
-                if (tr >= 0 && kidx < nK) {
-                    if (kidx < nSpan) {
-                        if (kidx <= tr) kd = (kidx >= tr - w + 1) ? 1 : 2;
-                    } else {
-                        kd = 1;
-                    }
-                }
-                kind[j] = kd;
+                const int kspan = kidx <= tr ? (kidx >= tr - w + 1 ? 1 : 2) : 0;
+                kind[j] = (tr >= 0 && kidx < nK) ? (kidx < nSpan ? kspan : 1) : 0;
                 lg[j] = tau * sT[rt][tt][i];
-                if (kd == 1) bmax = fmaxf(bmax, lg[j]);
+                bmax = fmaxf(bmax, kind[j] == 1 ? lg[j] : -INFINITY);
             }
             bmax = quad_max(bmax);
             const float mnew = fmaxf(mrun[rt], bmax);
@@ -334,9 +332,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const int j = hh * 8 + jj, tt = j >> 2, i = j & 3;
-                    float pv_ = 0.f;
-                    if (kind[j] == 1) pv_ = __expf(lg[j] - mnew);
-                    else if (kind[j] == 2) pv_ = kT[rt][tt][i] * elin;
+                    const float e1 = __expf(lg[j] - mnew), e2 = kT[rt][tt][i] * elin;
+                    const float pv_ = kind[j] == 1 ? e1 : (kind[j] == 2 ? e2 : 0.f);
                     Zp[rt] += pv_;
                     u[jj] = bf16_bits(pv_);
                 }
