@@ -153,7 +153,7 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
     if constexpr (sizeof(T) == 2) {
         const int wpi = (d.G * d.L + kOutRows - 1) / kOutRows;
-        const size_t olds = out_smem(D, F, d.C).total;
+        const size_t olds = out_smem<D, F>(d.C).total;
         if (allow_lds(output_kernel_bf16<D, F>, olds) != hipSuccess) return LOLA_ERR_HIP;
         hipLaunchKernelGGL((output_kernel_bf16<D, F>), dim3(a.NI * wpi, chains), dim3(kOutThreads), olds, s, a);
     } else {

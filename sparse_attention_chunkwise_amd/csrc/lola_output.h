@@ -30,17 +30,19 @@ struct OutSmem {
     size_t sP, refs, Wl, Hs, Ks, VT, Pk, total;
 };
 
-__host__ __device__ inline OutSmem out_smem(int D, int F, int C)
+// The cache references come last: every other offset is a compile-time constant.
+template <int D, int F>
+__host__ __device__ constexpr OutSmem out_smem(int C)
 {
-    OutSmem m;
+    OutSmem m{};
     size_t off = 0;
     m.sP = off;   off += align_up(sizeof(float) * F, 16);
-    m.refs = off; off += align_up(sizeof(int) * (size_t)(C > 0 ? C : 1), 16);
     m.Wl = off;   off += align_up(sizeof(uint16_t) * 2 * (size_t)(F / 2) * (D + 8), 16);  // W hi, lo [2][Fh][D+8]
     m.Hs = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);            // H_c^T [D][F+8]
     m.Ks = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (D + 8);
     m.VT = off;   off += sizeof(uint16_t) * (size_t)D * (kKeyBlock + 8);
     m.Pk = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (F + 8);
+    m.refs = off; off += align_up(sizeof(int) * (size_t)(C > 0 ? C : 1), 16);
     m.total = align_up(off, 16);
     return m;
 }
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     constexpr int KP = D + 8, VP = KB + 8, PP = F + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
-    const OutSmem sm = out_smem(D, F, d.C);
+    constexpr OutSmem sm = out_smem<D, F>(1);  // every offset used here is independent of C
     float* sP = (float*)(smem + sm.sP);
     int* srefL = (int*)(smem + sm.refs);
     uint16_t* Ks = (uint16_t*)(smem + sm.Ks);
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             pk[k] = kidx < nK ? k4 : make_uint4(0, 0, 0, 0);                                                         \
         }                                                                                                            \
         if (tid < VPU) {                                                                                             \
-            const int pr = tid / (D / 8), un = tid % (D / 8);                                                        \
+            const int pr = tid % (KB / 2), un = tid / (KB / 2);                                                      \
             _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
                 const int kidx = (BASE) + 2 * pr + k, kc = kidx < nK ? kidx : 0;                                     \
                 const int rf = sref[kc >= nSpan ? kc - nSpan : 0];                                                   \
@@ -255,8 +257,10 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             if (idx < KB * D / 8) *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
         }
         if (tid < VPU) {
-            // keys 2pr, 2pr+1 sit next to each other in the operand order of their half
-            const int pr = tid / (D / 8), un = tid % (D / 8), kc = (2 * pr / 32) * 32 + key_perm((2 * pr) % 32);
+            // keys 2pr, 2pr+1 sit next to each other in the operand order of their half.
+            // A wave covers 32 key pairs x 2 value units: its lanes write one row at a
+            // time into distinct dwords (units 8 rows apart would share an LDS bank).
+            const int pr = tid % (KB / 2), un = tid / (KB / 2), kc = (2 * pr / 32) * 32 + key_perm((2 * pr) % 32);
             const uint32_t w0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w}, w1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
