@@ -168,7 +168,7 @@ template <int D, int F, typename T>
 lola_status launch_decode(Args& a, hipStream_t s)
 {
     if constexpr (sizeof(T) == 2) {
-        const size_t lds = dec_smem(D, F, a.d.C).total;
+        const size_t lds = dec_smem<D, F>(a.d.C).total;
         if (allow_lds(decode_kernel_bf16<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
         hipLaunchKernelGGL((decode_kernel_bf16<D, F>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
     } else {

@@ -31,22 +31,25 @@ struct DecSmem {
     size_t HhT, HlT, Wl, sP, cposL, esc, phiE, phiF, xrow, stVT, misc, total;
 };
 
-__host__ __device__ inline DecSmem dec_smem(int D, int F, int C)
+// The two arrays sized by the cache capacity come last: every other offset is a
+// compile-time constant.
+template <int D, int F>
+__host__ __device__ constexpr DecSmem dec_smem(int C)
 {
-    DecSmem m;
+    DecSmem m{};
     const int Cp = C > 0 ? C : 1;
     size_t off = 0;
     m.HhT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
     m.HlT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
     m.Wl = off;    off += align_up(sizeof(uint16_t) * 3 * (size_t)(F / 2) * (D + 8), 16);  // W parts, padded rows
     m.sP = off;    off += align_up(sizeof(float) * F, 16);
-    m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
-    m.esc = off;   off += align_up(sizeof(float) * (size_t)(C + 1), 16);
     m.phiE = off;  off += align_up(sizeof(float) * F, 16);
     m.phiF = off;  off += align_up(sizeof(float) * F, 16);
     m.xrow = off;  off += align_up(sizeof(float) * D, 16);
     m.stVT = off;  off += align_up(sizeof(uint16_t) * (size_t)D * (kDecBlock + 8), 16);
-    m.misc = off;  off += sizeof(int) * 16;
+    m.misc = off;  off += align_up(sizeof(int) * 16, 16);
+    m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
+    m.esc = off;   off += align_up(sizeof(float) * (size_t)(Cp + 1), 16);
     m.total = align_up(off, 16);
     return m;
 }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int G = d.G, w = d.w, C = d.C;
-    const DecSmem sm = dec_smem(D, F, C);
+    const DecSmem sm = dec_smem<D, F>(C);  // only the last two offsets depend on C
     uint16_t* HhT = (uint16_t*)(smem + sm.HhT);
     uint16_t* HlT = (uint16_t*)(smem + sm.HlT);
     float* sP = (float*)(smem + sm.sP);
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         // this wave's keys base + wave * KW + tt * 16 + r16 as MFMA fragments, straight
         // from memory (a lane's 16 bytes are contiguous in the key row)
         constexpr int VN = (KBL / 2) * (D / 8) / 256;
+        static_assert((KBL / 2) * (D / 8) % 256 == 0, "V units cover the key block exactly");
         uint4 kq[2][DS], vq0[VN], vq1[VN];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -445,13 +449,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
-            const int idx = tid + k * 256, k0 = base + 2 * (idx / (D / 8)), un = idx % (D / 8);
+            const int idx = tid + k * 256, k0 = base + 2 * (idx % (KBL / 2)), un = idx / (KBL / 2);
             vq0[k] = *(const uint4*)(key_row(k0 < nK ? k0 : nK - 1, true) + un * 8);
             vq1[k] = *(const uint4*)(key_row(k0 + 1 < nK ? k0 + 1 : nK - 1, true) + un * 8);
         }
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
-            const int idx = tid + k * 256, pr = idx / (D / 8), un = idx % (D / 8);
+            // a wave covers 64 key pairs of one value unit: each transposed store puts its
+            // lanes on distinct dwords of one row (units 8 rows apart share an LDS bank)
+            const int idx = tid + k * 256, pr = idx % (KBL / 2), un = idx / (KBL / 2);
             const int k0 = base + 2 * pr, k1 = k0 + 1;
             const uint4 v0 = k0 < nK ? vq0[k] : make_uint4(0, 0, 0, 0);
             const uint4 v1 = k1 < nK ? vq1[k] : make_uint4(0, 0, 0, 0);
