@@ -226,6 +226,22 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ch.tok();
     const int cnt0 = min(max(ch.cnt(), 0), C);
+    // W (three bf16 parts) goes to LDS once per workgroup, every load issued before
+    // any is waited for; the four waves then read their MFMA operands from there
+    constexpr int WP = D + 8, WN = 3 * Fh * D / 8 / 256;  // padded row, 16-byte pieces per thread
+    static_assert(3 * Fh * D % (8 * 256) == 0, "W pieces cover the workgroup exactly");
+    __shared__ __attribute__((aligned(16))) uint16_t Wl[3 * Fh * WP];
+    const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
+    {
+        uint4 w4[WN];
+#pragma unroll
+        for (int k = 0; k < WN; ++k) w4[k] = *(const uint4*)(Wb + (size_t)(tid + k * 256) * 8);
+#pragma unroll
+        for (int k = 0; k < WN; ++k) {
+            const int e = (tid + k * 256) * 8;  // row = part * Fh + feature
+            *(uint4*)(Wl + (e / D) * WP + e % D) = w4[k];
+        }
+    }
     if (blockIdx.x == 0 && tid == 0 && g == 0) ((int64_t*)(a.ws + a.wl.t0))[b] = t0;
     if (blockIdx.x == 0 && tid < 16) ((uint32_t*)(a.ws + a.wl.xsync))[chain * 16 + tid] = 0u;
     {
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks)
         xb[ks] = __builtin_bit_cast(bf16x8, src ? *(const uint4*)(src + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0));
-    const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
+    __syncthreads();  // W in LDS
     floatx4 zt[FTH];
 #pragma unroll
     for (int ft = 0; ft < FTH; ++ft) {
@@ -280,8 +296,7 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
 #pragma unroll
             for (int part = 0; part < 3; ++part)
                 zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    *(const bf16x8*)(Wb + (size_t)part * Fh * D + (ft * 16 + r16) * D + ks * 32 + qg * 8), xb[ks], zt[ft],
-                    0, 0, 0);
+                    *(const bf16x8*)(Wl + (part * Fh + ft * 16 + r16) * WP + ks * 32 + qg * 8), xb[ks], zt[ft], 0, 0, 0);
     }
     float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
