@@ -81,7 +81,8 @@ typedef struct {
 
 /* Bytes of the state buffer for `batch` sequences (header, tokens seen, W,
  * and per (sequence, KV head): H [F][D] f32, s [F] f32, cache positions,
- * window ring and cache keys/values).  0 if the config is not supported. */
+ * window ring and cache keys/values, and for bf16 io the feature rows of the
+ * cached keys).  0 if the config is not supported. */
 size_t lola_state_bytes(const lola_config* cfg, int32_t batch);
 
 /* Bytes of scratch that lola_prefill_chunk needs for up to `max_tokens`

@@ -221,42 +221,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
     __syncthreads();  // W parts and H in LDS
-    // SRE of P tiles of 16 candidates (candidate r16 of tile p: key fragments kb[p],
-    // values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p] whether it is one):
-    // n^T = H^T phi^T with H and phi in bf16 hi/lo parts (hi.hi + lo.hi + hi.lo;
-    // the H operands are read once for all P tiles), d = s . phi, e = |n / d - v|^2
-    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
-                         float* phi0 = nullptr) {  // phi0: phi of candidate 0 of tile 0, natural order
+    // Error of P tiles of 16 candidates from their feature operands (bf16 hi, lo
+    // parts bh, bl; candidate r16 of tile p) and 1 / d: n^T = H^T phi^T with H and phi
+    // in hi/lo parts (hi.hi + lo.hi + hi.lo; the H operands are read once for all P
+    // tiles), e = |n / d - v|^2 (values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p]
+    // whether the column is a candidate)
+    auto sre_core = [&](auto pTag, const bf16x8 (*bh)[FM], const bf16x8 (*bl)[FM], const float* inv, const bool* cv,
+                        const uint2 (*vq)[DT], float* e) {
         constexpr int P = decltype(pTag)::value;
-        bf16x8 bh[P][FM], bl[P][FM];
-        float inv[P];
-        {
-            float x[P][F / 4];
-            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
-            if (phi0 && r16 == 0)
-#pragma unroll
-                for (int h = 0; h < F / 4; ++h) phi0[slot_feature(h, qg)] = x[0][h];
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                float dd = 0.f;
-#pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    u16x8 uh, ul;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float xv = x[p][mf * 8 + j];
-                        const uint16_t h = bf16_bits(xv);
-                        uh[j] = h;
-                        ul[j] = bf16_bits(xv - bf16_val(h));
-                        dd += xv * sP[mf * 32 + qg * 8 + j];
-                    }
-                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
-                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
-                }
-                dd = quad_sum(dd);
-                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
-            }
-        }
         float es[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) es[p] = 0.f;
@@ -293,6 +265,51 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             es[p] = quad_sum(es[p]);
             e[p] = es[p];
         }
+    };
+    // 1 / d with d = s . (phi hi + phi lo): the feature values the MFMAs see (the
+    // prefill scan scores with the same 16-bit features)
+    auto inv_d = [&](const bf16x8* bh, const bf16x8* bl) -> float {
+        float dd = 0.f;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            const u16x8 uh = __builtin_bit_cast(u16x8, bh[mf]), ul = __builtin_bit_cast(u16x8, bl[mf]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dd += (bf16_val(uh[j]) + bf16_val(ul[j])) * sP[mf * 32 + qg * 8 + j];
+        }
+        dd = quad_sum(dd);
+        return dd > 0.f ? 1.f / dd : 0.f;
+    };
+    // SRE of P tiles whose features are computed here from the key fragments kb[p]
+    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
+                         float* phi0 = nullptr) {  // phi0: phi of candidate 0 of tile 0, natural order
+        constexpr int P = decltype(pTag)::value;
+        bf16x8 bh[P][FM], bl[P][FM];
+        float inv[P];
+        {
+            float x[P][F / 4];
+            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
+            if (phi0 && r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) phi0[slot_feature(h, qg)] = x[0][h];
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+#pragma unroll
+                for (int mf = 0; mf < FM; ++mf) {
+                    u16x8 uh, ul;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float xv = x[p][mf * 8 + j];
+                        const uint16_t h = bf16_bits(xv);
+                        uh[j] = h;
+                        ul[j] = bf16_bits(xv - bf16_val(h));
+                    }
+                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
+                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
+                }
+                inv[p] = inv_d(bh[p], bl[p]);
+            }
+        }
+        sre_core(pTag, bh, bl, inv, cv, vq, e);
     };
 
     // phi of the leaving key (wave 3, column 0 of a tile) and, when a pair must be
@@ -556,14 +573,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     //      previous tiles are scored ----
     if (hasE && nU > C) {
         const int nT = (cnt + 15) / 16;
-        uint4 kq[2][DS];
+        // features of the cached keys come from the state (hi | lo rows in operand order)
+        uint4 fq[2][2 * FM];
         uint2 vq[2][DT];
         auto tile_load = [&](int p, int tt) {
             const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
-            const bf16* kr = ch.cache_k<bf16>() + (size_t)slot * D;
+            const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
             const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) kq[p][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
+            for (int mf = 0; mf < FM; ++mf) {
+                fq[p][mf] = *(const uint4*)(pr + mf * 32);
+                fq[p][FM + mf] = *(const uint4*)(pr + F + mf * 32);
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vq[p][dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
         };
@@ -573,23 +594,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         if (wave + NW < nT) tile_load(1, wave + NW);
         for (int t0 = wave; t0 < nT; t0 += 2 * NW) {
             const int tl[2] = {t0, t0 + NW};
-            bf16x8 kb[2][DS];
+            bf16x8 bh[2][FM], bl[2][FM];
+            float inv[2];
             bool cv[2];
             uint2 vv[2][DT];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 cv[p] = tl[p] * 16 + r16 < cnt;
 #pragma unroll
-                for (int ks = 0; ks < DS; ++ks)
-                    kb[p][ks] = __builtin_bit_cast(bf16x8, cv[p] ? kq[p][ks] : make_uint4(0, 0, 0, 0));
+                for (int mf = 0; mf < FM; ++mf) {
+                    bh[p][mf] = __builtin_bit_cast(bf16x8, cv[p] ? fq[p][mf] : make_uint4(0, 0, 0, 0));
+                    bl[p][mf] = __builtin_bit_cast(bf16x8, cv[p] ? fq[p][FM + mf] : make_uint4(0, 0, 0, 0));
+                }
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vv[p][dt] = vq[p][dt];
             }
             if (t0 + 2 * NW < nT) tile_load(0, t0 + 2 * NW);
             if (t0 + 3 * NW < nT) tile_load(1, t0 + 3 * NW);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) inv[p] = inv_d(bh[p], bl[p]);
             float e[2];
-            if (tl[1] < nT) sre_tiles(std::integral_constant<int, 2>{}, kb, cv, vv, e);  // wave-uniform
-            else sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vv, e);
+            if (tl[1] < nT) sre_core(std::integral_constant<int, 2>{}, bh, bl, inv, cv, vv, e);  // wave-uniform
+            else sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, cv, vv, e);
 #pragma unroll
             for (int p = 0; p < 2; ++p)
                 if (tl[p] < nT && qg == 0 && cv[p]) esc[tl[p] * 16 + r16] = e[p];
@@ -622,18 +648,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         // phi of the folded key (wave 0, column 0 of a tile) and its value (wave 1),
         // then H += phi v^T, s += phi
         if (wave == 0) {
-            const bf16* kr = victim < cnt ? ch.cache_k<bf16>() + (size_t)victim * D : kE;
-            bf16x8 kb[DS];
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                const uint4 u4 = r16 == 0 ? *(const uint4*)(kr + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
-                kb[ks] = __builtin_bit_cast(bf16x8, u4);
-            }
-            float x[1][F / 4];
-            phi_tiles<D, F, 1>(Wl, &kb, r16, qg, x);
-            if (r16 == 0)
-#pragma unroll
-                for (int h = 0; h < F / 4; ++h) phiF[slot_feature(h, qg)] = x[0][h];
+            // the folded key's features: its stored row (hi + lo), or the leaving key's
+            if (victim < cnt) {
+                const uint16_t* pr = ch.cphi() + (size_t)victim * 2 * F;
+                for (int f = lane; f < F; f += 64) {
+                    const int q = perm_pos(f);
+                    phiF[f] = bf16_val(pr[q]) + bf16_val(pr[F + q]);
+                }
+            } else
+                for (int f = lane; f < F; f += 64) phiF[f] = phiE[f];
         } else if (wave == 1) {
             const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
             for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
@@ -664,11 +687,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         if (nU <= C) slot = cnt;
         else if (victim < cnt) slot = victim;
     }
-    if (slot >= 0)
+    if (slot >= 0) {
         for (int j = tid; j < D; j += 256) {
             ch.cache_k<bf16>()[(size_t)slot * D + j] = kE[j];
             ch.cache_v<bf16>()[(size_t)slot * D + j] = vE[j];
         }
+        uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F;  // its features: hi | lo, operand order
+        for (int f = tid; f < F; f += 256) {
+            const float x = phiE[f];
+            const uint16_t h = bf16_bits(x);
+            pr[perm_pos(f)] = h;
+            pr[F + perm_pos(f)] = bf16_bits(x - bf16_val(h));
+        }
+    }
     __syncthreads();
     if (w > 0)
         for (int j = tid; j < D; j += 256) {

@@ -19,7 +19,7 @@ constexpr int kMaxCache = 1024;
 constexpr int kMaxChunk = 256;
 constexpr int kMaxCand = kMaxCache + kMaxChunk;  // |cache| + |leaving keys| per interval
 constexpr uint32_t kMagic = 0x414c4f4cu;         // "LOLA"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 
 constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -61,13 +61,16 @@ struct StateHeader {
 
 // State buffer: header | W [Hkv][Fh][D] f32 | Wb [Hkv][3][Fh][D] bf16 (three parts of W, largest first) | chains [B][Hkv]
 // chain: tokens seen i64 | cache_count i32 | H^T [D][F] f32 | s [F] f32 | cache_pos [C] i32 |
-//        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io
+//        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io |
+//        cache_phi [C][2F] bf16 (bf16 io only: phi of each cached key as hi and lo parts,
+//        each in MFMA operand order, so that a decode step scores the cache without
+//        recomputing the feature map)
 // Every chain keeps its own token count so that concurrent chains of one
 // sequence never race on a shared counter.  The window ring slot of
 // position p is p % w.
 struct StateLayout {
     size_t W, Wb, chains, chain_bytes;
-    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v;
+    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi;
     size_t total;
 };
 
@@ -90,6 +93,7 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     s.oring_v = c;   c = align_up(c + (size_t)d.esize * d.w * d.D, 256);
     s.ocache_k = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
     s.ocache_v = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
+    s.ocphi = c;     c = align_up(c + (d.io == 1 ? sizeof(uint16_t) * 2 * (size_t)d.F * d.C : 0), 256);
     s.chain_bytes = c;
     s.total = s.chains + c * (size_t)B * d.Hkv;
     return s;

@@ -20,6 +20,8 @@
 // outer products, combine linear + cache + window attention).
 #pragma once
 
+#include <type_traits>
+
 #include "lola_internal.h"
 
 namespace lola {
@@ -39,6 +41,7 @@ struct Chain {
     template <typename T> __device__ T* ring_v() const { return (T*)(base + sl->oring_v); }
     template <typename T> __device__ T* cache_k() const { return (T*)(base + sl->ocache_k); }
     template <typename T> __device__ T* cache_v() const { return (T*)(base + sl->ocache_v); }
+    __device__ uint16_t* cphi() const { return (uint16_t*)(base + sl->ocphi); }  // bf16 io
 };
 
 __device__ __forceinline__ Chain chain_of(const Args& a, int chain)
@@ -924,6 +927,14 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
             const uint4 v4 = *(const uint4*)(xrow_v<T>(a, chain, b, g, code) + pc);
             *(uint4*)(ch.cache_k<T>() + (size_t)i * D + pc) = k4;
             *(uint4*)(ch.cache_v<T>() + (size_t)i * D + pc) = v4;
+        }
+    }
+    if constexpr (std::is_same<T, bf16>::value) {
+        // feature rows (hi | lo, operand order) of the cache entries added in this call
+        constexpr int PP = 2 * F / 8;
+        for (int q = tid; q < cnt * PP; q += NT) {
+            const int i = q / PP, pc = (q % PP) * 8, code = cref[i];
+            if (code >= 0) *(uint4*)(ch.cphi() + (size_t)i * 2 * F + pc) = *(const uint4*)(ws_phiS(a, chain, code) + pc);
         }
     }
     if (w > 0) {

@@ -895,6 +895,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 *(uint4*)(ch.cache_v<bf16>() + (size_t)i * D + pc) = v4;
             }
         }
+        // and their feature rows (hi | lo, operand order), for the decode step's scoring
+        constexpr int PP = 2 * F / 8;
+        for (int q = tid; q < nrc * PP; q += NT) {
+            const int i = rank + nb * (q / PP), pc = (q % PP) * 8, code = cref[i];
+            if (code >= 0) *(uint4*)(ch.cphi() + (size_t)i * 2 * F + pc) = *(const uint4*)(code_phs(code) + pc);
+        }
         if (w > 0) {
             const int64_t tend = t0 + n;
             const int64_t p0 = tend - w > t0 ? tend - w : t0;
