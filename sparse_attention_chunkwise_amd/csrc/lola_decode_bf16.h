@@ -447,16 +447,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     const float tau = d.tau;
 
     const int nblk = (nK + KBL - 1) / KBL;
-    for (int bi = 0; bi < nblk; ++bi) {
-        const int base = bi * KBL;
-        __syncthreads();  // previous block consumed
-        // every load of the block is issued before any is waited for; rows past nK
-        // load the last key and are zeroed
-        // this wave's keys base + wave * KW + tt * 16 + r16 as MFMA fragments, straight
-        // from memory (a lane's 16 bytes are contiguous in the key row)
-        constexpr int VN = (KBL / 2) * (D / 8) / 256;
-        static_assert((KBL / 2) * (D / 8) % 256 == 0, "V units cover the key block exactly");
-        uint4 kq[2][DS], vq0[VN], vq1[VN];
+    // Block bi + 1's key fragments and value rows load while block bi is scored; rows
+    // past nK load the last key and are zeroed.  A wave takes keys base + wave * KW +
+    // tt * 16 + r16 as MFMA fragments straight from memory (a lane's 16 bytes are
+    // contiguous in the key row).
+    constexpr int VN = (KBL / 2) * (D / 8) / 256;
+    static_assert((KBL / 2) * (D / 8) % 256 == 0, "V units cover the key block exactly");
+    uint4 kq[2][DS], vq0[VN], vq1[VN];
+    auto issue = [&](int base) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int kidx = base + wave * KW + tt * 16 + r16;
@@ -470,6 +468,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             vq0[k] = *(const uint4*)(key_row(k0 < nK ? k0 : nK - 1, true) + un * 8);
             vq1[k] = *(const uint4*)(key_row(k0 + 1 < nK ? k0 + 1 : nK - 1, true) + un * 8);
         }
+    };
+    if (nK > 0) issue(0);
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int base = bi * KBL;
+        __syncthreads();  // previous block consumed
+        uint4 kcur[2][DS];  // this block's fragments (kq is refilled below)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) kcur[tt][ks] = kq[tt][ks];
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
             // a wave covers 64 key pairs of one value unit: each transposed store puts its
@@ -487,7 +495,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 *(uint32_t*)(stVT + (un * 8 + j) * VP + kc) = lo | (hi << 16);
             }
         }
-        __syncthreads();
+        if (bi + 1 < nblk) issue(base + KBL);
+        lds_sync();  // V^T staged; the next block's loads stay in flight
         // this wave's 32 keys: base + wave*32 + tt*16 + r16
         const int kb0 = base + wave * KW;
         if (kb0 >= nK) continue;
@@ -498,7 +507,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             sT[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) {
-                kfr[tt][ks] = __builtin_bit_cast(bf16x8, kb0 + tt * 16 + r16 < nK ? kq[tt][ks] : make_uint4(0, 0, 0, 0));
+                kfr[tt][ks] = __builtin_bit_cast(bf16x8, kb0 + tt * 16 + r16 < nK ? kcur[tt][ks] : make_uint4(0, 0, 0, 0));
                 sT[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[tt][ks], qf[ks], sT[tt], 0, 0, 0);
             }
         }

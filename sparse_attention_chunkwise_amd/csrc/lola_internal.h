@@ -37,6 +37,17 @@ constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + 
                                                         false, false);                          \
         return OP(__uint_as_float(b[0]), __uint_as_float(b[1]));                                \
     }
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // lgkmcnt(0)
+
+// Block barrier that orders LDS only: global loads stay in flight across it
+// (a full __syncthreads would wait for every outstanding load and store).
+__device__ __forceinline__ void lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float lola_add(float a, float b) { return a + b; }
 LOLA_QUAD_COMBINE(quad_sum, lola_add)
 LOLA_QUAD_COMBINE(quad_max, fmaxf)

@@ -74,17 +74,6 @@ __host__ __device__ constexpr SplitSmem split_smem()
 // groups per column slice.
 __host__ __device__ inline int split_blocks(int D, int chains, int PU) { return 8 * (D / 16) * PU * ((chains + 7) / 8); }
 
-__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // lgkmcnt(0)
-
-// Block barrier that orders LDS only: global loads stay in flight across it
-// (a full __syncthreads would wait for every outstanding load and store).
-__device__ __forceinline__ void lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <int D, int F>
 __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
 {
