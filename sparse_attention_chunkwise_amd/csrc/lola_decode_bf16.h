@@ -546,8 +546,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
 
+    const bool scoreCache = hasE && nU > C;  // the SRE pass over the cache runs
+    const int nT = (cnt + 15) / 16;
+    // features of the cached keys come from the state (hi | lo rows in operand order)
+    uint4 fq[2][2 * FM];
+    uint2 vq[2][DT];
+    auto tile_load = [&](int p, int tt) {
+        const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
+        const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
+        const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            fq[p][mf] = *(const uint4*)(pr + mf * 32);
+            fq[p][FM + mf] = *(const uint4*)(pr + F + mf * 32);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vq[p][dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
+    };
+    // the wave's tiles wave, wave + NW, ... two at a time; the first two load while
+    // the attention parts are merged, the next two while the current two are scored
+    if (scoreCache && wave < nT) tile_load(0, wave);
+    if (scoreCache && wave + NW < nT) tile_load(1, wave + NW);
+
     // ---- merge the waves' softmax parts, add the linear part, store ----
-    __syncthreads();  // staging area becomes the merge area
+    // (LDS-only barriers: the first cache tiles' loads stay in flight)
+    lds_sync();  // staging area becomes the merge area
     {
         float* mM = mrg;                 // [NW][16]
         float* mZ = mrg + NW * 16;       // [NW][16]
@@ -559,7 +582,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mO[(wave * D + dt * 16 + qg * 4 + i) * 16 + r16] = O[dt][i];
-        __syncthreads();
+        lds_sync();
         for (int idx = tid; idx < G * D; idx += 256) {
             const int col = idx / D, dd = idx % D;
             float M = 0.f;
@@ -581,26 +604,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     //      the waves in turn; each tile's key and value rows are loaded while the
     //      previous tiles are scored ----
     if (hasE && nU > C) {
-        const int nT = (cnt + 15) / 16;
-        // features of the cached keys come from the state (hi | lo rows in operand order)
-        uint4 fq[2][2 * FM];
-        uint2 vq[2][DT];
-        auto tile_load = [&](int p, int tt) {
-            const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
-            const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
-            const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
-#pragma unroll
-            for (int mf = 0; mf < FM; ++mf) {
-                fq[p][mf] = *(const uint4*)(pr + mf * 32);
-                fq[p][FM + mf] = *(const uint4*)(pr + F + mf * 32);
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vq[p][dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
-        };
-        // the wave's tiles wave, wave + NW, ... two at a time; the next two load
-        // while the current two are scored
-        if (wave < nT) tile_load(0, wave);
-        if (wave + NW < nT) tile_load(1, wave + NW);
         for (int t0 = wave; t0 < nT; t0 += 2 * NW) {
             const int tl[2] = {t0, t0 + NW};
             bf16x8 bh[2][FM], bl[2][FM];
