@@ -172,6 +172,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         // W parts to LDS in batches of WB pieces (all loads of a batch issued before
         // any is stored; larger batches would need more registers than the wave has)
         constexpr int WB = WN % 4 == 0 ? 4 : (WN % 3 == 0 ? 3 : 1);
+        // H (from HBM, the longest wait) is requested first, all of it; the W batches
+        // (L2 hits) are stored to LDS while it is in flight
+        float4 hv4[HN];
+#pragma unroll
+        for (int k = 0; k < HN; ++k) hv4[k] = *(const float4*)(Hst + (size_t)(tid + k * 256) * 4);
 #pragma unroll
         for (int k0 = 0; k0 < WN; k0 += WB) {
             uint4 w4[WB];
@@ -184,27 +189,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        constexpr int HB = HN % 8 == 0 ? 8 : HN;  // H in batches of HB float4 per thread
 #pragma unroll
-        for (int k0 = 0; k0 < HN; k0 += HB) {
-            float4 hv4[HB];
+        for (int k = 0; k < HN; ++k) {
+            const int i = tid + k * 256, dd = (i * 4) / F, f = (i * 4) % F;
+            const float vv[4] = {hv4[k].x, hv4[k].y, hv4[k].z, hv4[k].w};
+            uint16_t h[4], l[4];
 #pragma unroll
-            for (int k = 0; k < HB; ++k) hv4[k] = *(const float4*)(Hst + (size_t)(tid + (k0 + k) * 256) * 4);
-#pragma unroll
-            for (int k = 0; k < HB; ++k) {
-                const int i = tid + (k0 + k) * 256, dd = (i * 4) / F, f = (i * 4) % F;
-                const float vv[4] = {hv4[k].x, hv4[k].y, hv4[k].z, hv4[k].w};
-                uint16_t h[4], l[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j] = bf16_bits(vv[j]);
-                    l[j] = bf16_bits(vv[j] - bf16_val(h[j]));
-                }
-                const int o = dd * HP + perm_pos(f);  // four consecutive features stay consecutive
-                *(uint2*)(HhT + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-                *(uint2*)(HlT + o) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+            for (int j = 0; j < 4; ++j) {
+                h[j] = bf16_bits(vv[j]);
+                l[j] = bf16_bits(vv[j] - bf16_val(h[j]));
             }
-            __builtin_amdgcn_sched_barrier(0);
+            const int o = dd * HP + perm_pos(f);  // four consecutive features stay consecutive
+            *(uint2*)(HhT + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            *(uint2*)(HlT + o) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
         }
         for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = ch.s()[i];
         for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
