@@ -195,6 +195,27 @@ def test_decode_steps(name, layer, B, T, steps):
     assert eh <= tol and es <= tol
 
 
+def test_decode_after_one_block_scan(monkeypatch):
+    """Decode steps on a state prefilled by the one-workgroup bf16 scan: its state-out
+    must also leave the cached keys' feature rows that a decode step scores with."""
+    name, layer, B, T, steps = DECODE_EDGE[-1]
+    W, Q, K, V = I.random_case(500 + len(name), layer, B, T + steps)
+    st = Stepper(layer, B, W)
+    tol = tol_for(layer)
+    monkeypatch.setenv("LOLA_SCAN_SPLIT", "0")
+    for a in range(0, T, layer.chunk):
+        e = min(a + layer.chunk, T)
+        g, r = st.step(Q[:, a:e], K[:, a:e], V[:, a:e])
+        assert row_rel_err(g, r) <= tol
+    monkeypatch.delenv("LOLA_SCAN_SPLIT")
+    for t in range(T, T + steps):
+        g, r = st.step(Q[:, t:t + 1], K[:, t:t + 1], V[:, t:t + 1], decode=True)
+        err = row_rel_err(g, r)
+        assert err <= tol, f"{name} one-block prefill, decode step {t}: {err:.3g}"
+    eh, es = st.compare_state()
+    assert eh <= tol and es <= tol
+
+
 def test_decode_equals_one_token_prefill():
     """lola_decode_step and lola_prefill_chunk(n=1) agree on outputs and state."""
     layer = I.LayerConfig(8, 2, 128, 64, 16, 24, 32, "bf16")
