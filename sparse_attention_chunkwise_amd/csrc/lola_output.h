@@ -27,7 +27,7 @@ constexpr int kKeyBlock = 64;
 constexpr int kOutThreads = 512;  // 8 waves x 16 query rows
 
 struct OutSmem {
-    size_t sP, refs, Wl, Hs, Ks, VT, Pk, total;
+    size_t sP, refs, Wl, Hs, Ks, VT, Pk, rowK, rowV, total;
 };
 
 // The cache references come last: every other offset is a compile-time constant.
@@ -42,6 +42,8 @@ __host__ __device__ constexpr OutSmem out_smem(int C)
     m.Ks = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (D + 8);
     m.VT = off;   off += sizeof(uint16_t) * (size_t)D * (kKeyBlock + 8);
     m.Pk = off;   off += sizeof(uint16_t) * (size_t)kKeyBlock * (F + 8);
+    m.rowK = off; off += sizeof(void*) * 2 * kKeyBlock;  // K row addresses of two key blocks
+    m.rowV = off; off += sizeof(void*) * 2 * kKeyBlock;
     m.refs = off; off += align_up(sizeof(int) * (size_t)(C > 0 ? C : 1), 16);
     m.total = align_up(off, 16);
     return m;
@@ -66,6 +68,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     uint16_t* Pk = (uint16_t*)(smem + sm.Pk);
     uint16_t* Wl = (uint16_t*)(smem + sm.Wl);
     uint16_t* Hs = (uint16_t*)(smem + sm.Hs);
+    const bf16** rowK = (const bf16**)(smem + sm.rowK);
+    const bf16** rowV = (const bf16**)(smem + sm.rowV);
 
     const int G = d.G, L = d.L, w = d.w;
     const int chain = blockIdx.y, b = chain / d.Hkv, g = chain % d.Hkv;
@@ -221,24 +225,27 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     constexpr int VPU = (KB / 2) * (D / 8);         // (key pair, 8-value unit) items for V
     static_assert(VPU <= NT, "one V key-pair unit per thread at most");
     uint4 pk[KU], pv[2], pp[PU];
+    // Row addresses of the KB keys of block j go to table j % 2, written by one
+    // wave two blocks ahead of the prefetch that reads them.
+    auto fill_rows = [&](int j, int i) {
+        const int kidx = j * KB + i, kc = kidx < nK ? kidx : 0;
+        const int ref = kc < nSpan ? xs0 + kc : sref[kc - nSpan];
+        rowK[(j & 1) * KB + i] = ref_k<bf16>(a, chain, b, g, ref);
+        rowV[(j & 1) * KB + i] = ref_v<bf16>(a, chain, b, g, ref);
+    };
 #define LOLA_OUT_PREFETCH(BASE)                                                                                      \
     do {                                                                                                             \
+        const int tb = (((BASE) / KB) & 1) * KB;                                                                     \
         _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
             const int idx = tid + k * NT, kr = (idx / (D / 8)) % KB, un = idx % (D / 8);                             \
-            const int kidx = (BASE) + kr, kc = kidx < nK ? kidx : 0;                                                 \
-            const int rf = sref[kc >= nSpan ? kc - nSpan : 0];                                                       \
-            const bf16* kp = ref_k<bf16>(a, chain, b, g, kc < nSpan ? xs0 + kc : rf);                                \
-            const uint4 k4 = *(const uint4*)(kp + un * 8);                                                           \
-            pk[k] = kidx < nK ? k4 : make_uint4(0, 0, 0, 0);                                                         \
+            const uint4 k4 = *(const uint4*)(rowK[tb + kr] + un * 8);                                                \
+            pk[k] = (BASE) + kr < nK ? k4 : make_uint4(0, 0, 0, 0);                                                  \
         }                                                                                                            \
         if (tid < VPU) {                                                                                             \
             const int pr = tid % (KB / 2), un = tid / (KB / 2);                                                      \
             _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
-                const int kidx = (BASE) + 2 * pr + k, kc = kidx < nK ? kidx : 0;                                     \
-                const int rf = sref[kc >= nSpan ? kc - nSpan : 0];                                                   \
-                const bf16* vp = ref_v<bf16>(a, chain, b, g, kc < nSpan ? xs0 + kc : rf);                            \
-                const uint4 v4 = *(const uint4*)(vp + un * 8);                                                       \
-                pv[k] = kidx < nK ? v4 : make_uint4(0, 0, 0, 0);                                                     \
+                const uint4 v4 = *(const uint4*)(rowV[tb + 2 * pr + k] + un * 8);                                   \
+                pv[k] = (BASE) + 2 * pr + k < nK ? v4 : make_uint4(0, 0, 0, 0);                                      \
             }                                                                                                        \
         }                                                                                                            \
         _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
@@ -248,9 +255,12 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             pp[k] = want ? p4 : make_uint4(0, 0, 0, 0);                                                              \
         }                                                                                                            \
     } while (0)
+    if (tid < 2 * KB) fill_rows(tid / KB, tid % KB);
+    __syncthreads();  // tables of blocks 0 and 1
     if (nK > 0) LOLA_OUT_PREFETCH(0);
     for (int base = 0; base < nK; base += KB) {
-        __syncthreads();  // the previous block (or W) is no longer read
+        __syncthreads();  // the previous block (or W) and the table of block base / KB are no longer read
+        if (tid < KB && base + 2 * KB < nK) fill_rows(base / KB + 2, tid);
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
             const int idx = tid + k * NT, kr = idx / (D / 8), un = idx % (D / 8);
