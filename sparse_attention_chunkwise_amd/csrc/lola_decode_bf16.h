@@ -206,9 +206,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = ch.s()[i];
         for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
     }
-    // query frags (columns r16 < G), phi of the leaving key (wave 3)
+    // query frags (columns r16 < G); the leaving key's row (wave 3, column 0) and
+    // its value rows dt * 16 + 4 qg .. + 3 (waves 0 and 3)
     bf16x8 qf[DS];
+    uint4 kEq[DS];
+    uint2 vEq[DT];
     {
+        const bool le = hasE && (wave == 0 || wave == NW - 1);
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks)
+            kEq[ks] = (hasE && wave == NW - 1 && r16 == 0) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vEq[dt] = le ? *(const uint2*)(vE + dt * 16 + qg * 4) : make_uint2(0, 0);
         const bool qv = r16 < G;
         const bf16* qp = (const bf16*)a.q + ((size_t)b * d.Hq + g * G + (qv ? r16 : 0)) * D;
 #pragma unroll
@@ -309,21 +318,26 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         sre_core(pTag, bh, bl, inv, cv, vq, e);
     };
 
-    // phi of the leaving key (wave 3, column 0 of a tile) and, when a pair must be
-    // folded, its SRE against the step-start state
+    // Wave 3: phi of the leaving key (column 0 of a tile) and, when a pair must be
+    // folded, its SRE against the step-start state.  Meanwhile wave 0, the only wave
+    // that needs phi(q), computes it and the linear read O_lin^T = H^T phi(q)^T; the
+    // leaving key's share of the linear part is added once its features are in LDS.
     const int nU = cnt + (hasE ? 1 : 0);
+    floatx4 O[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun = 0.f, Zp = 0.f;
+    float xq[F / 4];  // wave 0: phi(q) of column r16, operand-slot order
+    float zq = 0.f;   // wave 0: s . phi(q)
     if (wave == NW - 1) {
         bf16x8 kb[1][DS];
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) {
-            const uint4 u4 = (r16 == 0 && hasE) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
-            kb[0][ks] = __builtin_bit_cast(bf16x8, u4);
-        }
+        for (int ks = 0; ks < DS; ++ks) kb[0][ks] = __builtin_bit_cast(bf16x8, kEq[ks]);
         if (hasE && nU > C) {
             const bool cv[1] = {r16 == 0};
             uint2 vq[1][DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vq[0][dt] = *(const uint2*)(vE + dt * 16 + qg * 4);
+            for (int dt = 0; dt < DT; ++dt) vq[0][dt] = vEq[dt];
             float e[1];
             sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vq, e, phiE);
             if (lane == 0) esc[cnt] = e[0];
@@ -334,13 +348,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
 #pragma unroll
                 for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
         }
-    }
-    __syncthreads();
-
-    // ---- phi(q) for the query columns: z^T = W Q^T with W hi + lo ----
-    bf16x8 pf[FM];
-    float zl;
-    {
+    } else if (wave == 0) {
+        // phi(q) for the query columns: z^T = W Q^T with W hi + lo
         floatx4 zt[Fh / 16];
 #pragma unroll
         for (int ft = 0; ft < Fh / 16; ++ft) {
@@ -359,70 +368,60 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
         zmax = quad_max(zmax);
         zmin = quad_min(zmin);
-        float hv[F / 4];
         float sp = 0.f, sn = 0.f;
 #pragma unroll
         for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float e1 = __expf(zt[ft][i] - zmax), e2 = __expf(zmin - zt[ft][i]);
-                hv[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
-                hv[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+                xq[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+                xq[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
                 sp += e1;
                 sn += e2;
             }
         sp = quad_sum(sp);
         sn = quad_sum(sn);
         const float isp = 1.f / sp, isn = 1.f / sn;
-        float z = 0.f, kap = 0.f;
+        bf16x8 pf[FM];
 #pragma unroll
         for (int mf = 0; mf < FM; ++mf) {
             u16x8 u;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int hidx = mf * 8 + j;
-                const float x = hv[hidx] * (hidx < Fh / 4 ? isp : isn);
-                u[j] = bf16_bits(x);
-                const int pp = mf * 32 + qg * 8 + j;  // operand position of this feature
-                z += x * sP[pp];
-                // feature index of operand position pp for phi of the leaving key (natural order)
-                const int ftile = 2 * mf + (j >> 2), fidx = ftile * 16 + qg * 4 + (j & 3);
-                kap += x * phiE[fidx];
+                xq[hidx] *= hidx < Fh / 4 ? isp : isn;
+                u[j] = bf16_bits(xq[hidx]);
+                zq += xq[hidx] * sP[mf * 32 + qg * 8 + j];  // operand position of this feature
             }
             pf[mf] = __builtin_bit_cast(bf16x8, u);
         }
-        z = quad_sum(z);
-        kap = quad_sum(kap);
-        if (!hasE) kap = 0.f;
-        zl = z + kap;
-        // the leaving key's linear weight per query column, for the linear read of wave 0
-        if (wave == 0 && qg == 0) phiF[r16] = kap;
-    }
-    __syncthreads();
-
-    // ---- linear read (wave 0): O_lin^T = H^T phi(q)^T ----
-    floatx4 O[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mrun = 0.f, Zp = 0.f;
-    if (wave == 0) {
+        zq = quad_sum(zq);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int mf = 0; mf < FM; ++mf)
                 O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(HhT + (dt * 16 + r16) * HP + mf * 32 + qg * 8),
                                                                 pf[mf], O[dt], 0, 0, 0);
-        // pending key: kappa * v_E, added to the linear part (weight e^-M, M floored at 0)
-        const float kap = phiF[r16];
+    }
+    __syncthreads();  // phi of the leaving key in LDS
+    if (wave == 0) {
+        // the leaving key's linear weight kappa = phi(q) . phi(k_E) per query column;
+        // kappa * v_E joins the linear part (weight e^-M, M floored at 0)
+        float kap = 0.f;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kap += xq[mf * 8 + j] * phiE[(2 * mf + (j >> 2)) * 16 + qg * 4 + (j & 3)];
+        kap = quad_sum(kap);
+        if (!hasE) kap = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            float vv[4];
-            if (hasE) load4(vE + dt * 16 + qg * 4, vv);
-            else vv[0] = vv[1] = vv[2] = vv[3] = 0.f;
+            const float vv[4] = {__uint_as_float(vEq[dt].x << 16), __uint_as_float(vEq[dt].x & 0xffff0000u),
+                                 __uint_as_float(vEq[dt].y << 16), __uint_as_float(vEq[dt].y & 0xffff0000u)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) O[dt][i] += kap * vv[i];
         }
-        Zp = qg == 0 ? zl : 0.f;
+        Zp = qg == 0 ? zq + kap : 0.f;
     }
 
     // ---- keys: window [ws0, t] then cache slots; blocks of 128, 32 per wave ----
