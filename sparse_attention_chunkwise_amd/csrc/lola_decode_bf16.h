@@ -632,6 +632,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     __syncthreads();
     int victim = -1;
     if (hasE && nU > C) {
+        // H (fp32) for the fold is requested before the victim is known
+        float* Hd = ch.H();
+        constexpr int HN = D * F / 4 / 256;  // float4 per thread
+        float4 h4[HN];
+#pragma unroll
+        for (int k = 0; k < HN; ++k) h4[k] = *(const float4*)(Hd + (size_t)(tid + k * 256) * 4);
         if (wave == 0) {
             // lowest SRE, newest position on a tie: minimise (bits(e), ~pos)
             unsigned long long best = ~0ull;
@@ -651,7 +657,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             for (int o = 32; o > 0; o >>= 1) vi = min(vi, __shfl_xor(vi, o, 64));
             if (lane == 0) misc[0] = vi;
         }
-        __syncthreads();
+        lds_sync();  // (LDS-only barriers up to the fold: H stays in flight)
         victim = misc[0];
         // phi of the folded key (wave 0, column 0 of a tile) and its value (wave 1),
         // then H += phi v^T, s += phi
@@ -669,12 +675,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
             for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
         }
-        __syncthreads();
-        float* Hd = ch.H();
-        constexpr int HN = D * F / 4 / 256;  // float4 per thread, all loaded before any is stored
-        float4 h4[HN];
-#pragma unroll
-        for (int k = 0; k < HN; ++k) h4[k] = *(const float4*)(Hd + (size_t)(tid + k * 256) * 4);
+        lds_sync();
 #pragma unroll
         for (int k = 0; k < HN; ++k) {
             const int i = (tid + k * 256) * 4, dd = i / F, f = i % F;
@@ -687,9 +688,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
         for (int f = tid; f < F; f += 256) ch.s()[f] += phiF[f];
     }
-    __syncthreads();
 
     // ---- cache slot, then the ring (the leaving pair lives in slot t % w) ----
+    // (the victim's rows were read before the barrier above; each thread reads the
+    // leaving pair's elements before it overwrites them, so no barrier waits for the
+    // H stores)
     int slot = -1;
     if (hasE) {
         if (nU <= C) slot = cnt;
@@ -708,7 +711,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             pr[F + perm_pos(f)] = bf16_bits(x - bf16_val(h));
         }
     }
-    __syncthreads();
     if (w > 0)
         for (int j = tid; j < D; j += 256) {
             ch.ring_k<bf16>()[(size_t)rs * D + j] = knew[j];
