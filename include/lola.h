@@ -121,6 +121,26 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
 
+/* lola_prefill_chunk with a token count per sequence, for batches whose
+ * sequences advance by different amounts in one call (prefill chunks of
+ * several lengths, single decode tokens, idle sequences).  The method runs
+ * independently per sequence (each (sequence, KV head) pair owns its window,
+ * cache and linear state; LoLA summary, "Methodologie: LoLA"), so sequence b
+ * gets exactly the result of lola_prefill_chunk over its own n_tokens[b]
+ * tokens, with its update intervals counted from its own start.
+ *   n_tokens: device [batch] int32, 4-byte aligned, read by the kernels; each
+ *             entry is clamped to [0, max_tokens] (0 leaves the sequence,
+ *             including its token count, unchanged)
+ *   q, k, v, out: laid out as for lola_prefill_chunk with max_tokens rows per
+ *             sequence; sequence b reads and writes its first n_tokens[b] rows,
+ *             the other rows of out are not written
+ *   workspace: at least lola_prefill_workspace_bytes(cfg, batch, max_tokens).
+ * Host-side checks as for lola_prefill_chunk (max_tokens > 0), plus
+ * LOLA_ERR_INVALID_ARG for a NULL or misaligned n_tokens. */
+lola_status lola_prefill_ragged(const lola_config* cfg, void* state, int32_t batch, int32_t max_tokens,
+                                const int32_t* n_tokens, const void* q, const void* k, const void* v,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One token for every sequence: identical in result to
  * lola_prefill_chunk(n_tokens = 1) (a one-token interval), in one fused launch
  * that needs no workspace.

@@ -210,6 +210,10 @@ Args base_args(const Dims& d, int B, void* state)
     return a;
 }
 
+lola_status prefill_impl(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens, const int32_t* seqn,
+                         const void* q, const void* k, const void* v, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events);
+
 }  // namespace
 
 extern "C" {
@@ -253,6 +257,27 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
                                      const void* q, const void* k, const void* v, void* out, void* workspace,
                                      size_t workspace_bytes, void* stream, void* const* events)
 {
+    return prefill_impl(cfg, state, batch, n_tokens, nullptr, q, k, v, out, workspace, workspace_bytes, stream,
+                        events);
+}
+
+lola_status lola_prefill_ragged(const lola_config* cfg, void* state, int32_t batch, int32_t max_tokens,
+                                const int32_t* n_tokens, const void* q, const void* k, const void* v, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!n_tokens || ((uintptr_t)n_tokens & 3u)) return LOLA_ERR_INVALID_ARG;
+    return prefill_impl(cfg, state, batch, max_tokens, n_tokens, q, k, v, out, workspace, workspace_bytes, stream,
+                        nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+lola_status prefill_impl(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens, const int32_t* seqn,
+                         const void* q, const void* k, const void* v, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events)
+{
     Dims d;
     lola_status st = make_dims(cfg, &d);
     if (st != LOLA_OK) return st;
@@ -273,8 +298,13 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
     a.k = k;
     a.v = v;
     a.out = out;
+    a.seqn = seqn;
     return dispatch_prefill(a, (hipStream_t)stream, events);
 }
+
+}  // namespace
+
+extern "C" {
 
 lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch, const void* q, const void* k,
                              const void* v, void* out, void* stream)

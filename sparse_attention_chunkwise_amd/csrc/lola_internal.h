@@ -238,7 +238,8 @@ __device__ __forceinline__ float wave_sum(float v)
 // Kernel argument bundle common to the launches.
 struct Args {
     Dims d;
-    int B, n, NI;
+    int B, n, NI;           // n: rows per sequence in q, k, v, out; NI: intervals of n tokens
+    const int32_t* seqn;    // device [B]: tokens of each sequence (<= n), or null: n for all
     unsigned char* state;
     unsigned char* ws;
     const void* q;
@@ -248,5 +249,14 @@ struct Args {
     StateLayout sl;
     WsLayout wl;
 };
+
+// Tokens sequence b consumes in this call: its entry of the per-sequence counts
+// clamped to [0, n], or n when the call has none.
+__device__ __forceinline__ int seq_tokens(const Args& a, int b)
+{
+    if (!a.seqn) return a.n;
+    const int v = a.seqn[b];
+    return v < 0 ? 0 : (v > a.n ? a.n : v);
+}
 
 }  // namespace lola

@@ -78,9 +78,11 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     const int c = blockIdx.x / wpi, rblk = blockIdx.x % wpi;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
     const int NI = a.NI;
+    const int ns = seq_tokens(a, b);
+    if ((int64_t)c * L >= ns) return;  // past this sequence's tokens (the whole workgroup)
     const int64_t t0 = ws_t0(a, b);
     const int64_t ap = t0 + (int64_t)c * L;
-    const int64_t ep = ap + L < t0 + a.n ? ap + L : t0 + a.n;
+    const int64_t ep = ap + L < t0 + ns ? ap + L : t0 + ns;
     const int Lc = (int)(ep - ap);
 
     // ---- stage s_c (operand order) and the cache refs of the snapshot ----

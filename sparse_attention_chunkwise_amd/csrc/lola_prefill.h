@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
     __shared__ float xs[4][D];
     const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int w = a.d.w, C = a.d.C, X = a.wl.X;
+    const int w = a.d.w, C = a.d.C, X = a.wl.X, ns = seq_tokens(a, b);
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ch.tok();
     const int cnt0 = min(max(ch.cnt(), 0), C);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
                     src = ch.ring_k<T>() + (size_t)slot * D;
                     srcv = ch.ring_v<T>() + (size_t)slot * D;
                 }
-            } else {
+            } else if (row - w < ns) {  // rows past this sequence's tokens stay zero
                 src = (const T*)a.k + (((size_t)b * a.n + (row - w)) * a.d.Hkv + g) * D;
             }
         } else if (row < X + C) {
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
     constexpr int F = 2 * Fh, FTH = Fh / 16, DS = D / 32;
     const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
-    const int w = a.d.w, C = a.d.C, X = a.wl.X, Cp = C > 0 ? C : 1;
+    const int w = a.d.w, C = a.d.C, X = a.wl.X, Cp = C > 0 ? C : 1, ns = seq_tokens(a, b);
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ch.tok();
     const int cnt0 = min(max(ch.cnt(), 0), C);
@@ -260,7 +260,9 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
             if (p < 0) return nullptr;
             return (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)(p % w) * D;
         }
-        if (row < X) return (const bf16*)(v ? a.v : a.k) + (((size_t)b * a.n + (row - w)) * a.d.Hkv + g) * D;
+        if (row < X)  // rows past this sequence's tokens: none
+            return row - w < ns ? (const bf16*)(v ? a.v : a.k) + (((size_t)b * a.n + (row - w)) * a.d.Hkv + g) * D
+                                : nullptr;
         if (row < X + C && row - X < cnt0) return (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (size_t)(row - X) * D;
         return nullptr;
     };
@@ -483,7 +485,8 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ws_t0(a, b);
-    const int n = a.n, NI = a.NI;
+    const int n = a.n, NI = a.NI;  // rows per sequence in k, v; snapshot slots per chain
+    const int ns = seq_tokens(a, b), NIs = (ns + L - 1) / L;  // this sequence's tokens and intervals
     const int Cp = C > 0 ? C : 1;
     const int U = C + L;
 
@@ -525,9 +528,9 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     int* snapRef = (int*)(a.ws + a.wl.snapRef) + (size_t)chain * NI * Cp;
     int* snapN = (int*)(a.ws + a.wl.snapN) + (size_t)chain * NI;
 
-    for (int c = 0; c < NI; ++c) {
+    for (int c = 0; c < NIs; ++c) {
         const int64_t ap = t0 + (int64_t)c * L;
-        const int64_t ep = ap + L < t0 + n ? ap + L : t0 + n;
+        const int64_t ep = ap + L < t0 + ns ? ap + L : t0 + ns;
 
         // ---- interval-start snapshot (H^T [D][F], s, cache refs) ----
         {
@@ -938,7 +941,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         }
     }
     if (w > 0) {
-        const int64_t tend = t0 + n;
+        const int64_t tend = t0 + ns;
         const int64_t p0 = tend - w > t0 ? tend - w : t0;
         const int nr = (int)(tend - p0);
         for (int q = tid; q < nr * NP; q += NT) {
@@ -952,7 +955,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     }
     if (tid == 0) {
         ch.cnt() = cnt;
-        ch.tok() = t0 + n;
+        ch.tok() = t0 + ns;
     }
 }
 
@@ -992,9 +995,11 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
     const int wpi = (rows + 63) / 64;
     const int c = blockIdx.x / wpi, rblk = blockIdx.x % wpi;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, qg = lane >> 4;
+    const int ns = seq_tokens(a, b);
+    if ((int64_t)c * L >= ns) return;  // past this sequence's tokens (the whole workgroup)
     const int64_t t0 = ws_t0(a, b);
     const int64_t ap = t0 + (int64_t)c * L;
-    const int64_t ep = ap + L < t0 + a.n ? ap + L : t0 + a.n;
+    const int64_t ep = ap + L < t0 + ns ? ap + L : t0 + ns;
     const int Lc = (int)(ep - ap);
     if (rblk * 64 + wave * 16 >= rows) return;  // whole wave idle (no block-level sync below)
 

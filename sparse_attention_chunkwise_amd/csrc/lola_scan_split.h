@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     Chain ch = chain_of(a, chain);
     const int64_t t0 = ws_t0(a, b);
-    const int n = a.n, NI = a.NI;
+    const int n = a.n, NI = a.NI;  // rows per sequence in k, v; snapshot slots per chain
+    const int ns = seq_tokens(a, b), NIs = (ns + L - 1) / L;  // this sequence's tokens and intervals
     const int Cp = C > 0 ? C : 1;
     const int U = C + L;
     uint32_t* xsync = (uint32_t*)(a.ws + a.wl.xsync) + (size_t)chain * 16;
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     };
     auto interval = [&](int c) -> Iv {
         const int64_t ap = t0 + (int64_t)c * L;
-        const int64_t ep = ap + L < t0 + n ? ap + L : t0 + n;
+        const int64_t ep = ap + L < t0 + ns ? ap + L : t0 + ns;
         Iv v;
         v.eS = ap - w > 0 ? ap - w : 0;
         const int64_t eE = ep - w;
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         prefetch_next(cnt + v0.nE, cnt, v0.xE0);
     }
 
-    for (int c = 0; c < NI; ++c) {
+    for (int c = 0; c < NIs; ++c) {
         const Iv iv = interval(c);
         const int64_t eS = iv.eS;
         const int nE = iv.nE, xE0 = iv.xE0;
@@ -480,8 +481,8 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         // ---- wave 0: exact top-C on (SRE desc, position asc), compaction, slot
         //      updates and the next interval's candidate list ----
         const int cntN = nU < C ? nU : C;
-        const Iv ivN = interval(c + 1 < NI ? c + 1 : c);
-        const int nUN = c + 1 < NI ? cntN + ivN.nE : 0;
+        const Iv ivN = interval(c + 1 < NIs ? c + 1 : c);
+        const int nUN = c + 1 < NIs ? cntN + ivN.nE : 0;
         uint32_t kbits = 0u;  // wave 0: bit i set = the lane's candidate of chunk i stays
         // Slot update (wave 0, while the fold rows load): folded cache pairs free their
         // slots in slot order, and the kept leaving keys take the freed slots in order,
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             if (code >= 0) *(uint4*)(ch.cphi() + (size_t)i * 2 * F + pc) = *(const uint4*)(code_phs(code) + pc);
         }
         if (w > 0) {
-            const int64_t tend = t0 + n;
+            const int64_t tend = t0 + ns;
             const int64_t p0 = tend - w > t0 ? tend - w : t0;
             const int nr = (int)(tend - p0);
             const int nrr = nr > rank ? (nr - rank + nb - 1) >> nbl : 0;
@@ -933,7 +934,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
     if (tid == 0) {
         ch.cnt() = cnt;
-        ch.tok() = t0 + n;
+        ch.tok() = t0 + ns;
     }
 }
 

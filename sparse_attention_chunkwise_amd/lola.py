@@ -22,7 +22,8 @@ _STATUS = {0: "LOLA_OK", -1: "LOLA_ERR_INVALID_ARG", -2: "LOLA_ERR_UNSUPPORTED",
 
 # Every symbol include/lola.h declares.
 EXPORTS = ("lola_state_bytes", "lola_prefill_workspace_bytes", "lola_init_state", "lola_prefill_chunk",
-           "lola_prefill_chunk_timed", "lola_decode_step", "lola_read_cache", "lola_check_state", "lola_status_string")
+           "lola_prefill_chunk_timed", "lola_prefill_ragged", "lola_decode_step", "lola_read_cache",
+           "lola_check_state", "lola_status_string")
 
 
 class LolaError(RuntimeError):
@@ -59,6 +60,8 @@ def lib():
         L.lola_prefill_chunk.restype = ctypes.c_int
         L.lola_prefill_chunk_timed.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.lola_prefill_chunk_timed.restype = ctypes.c_int
+        L.lola_prefill_ragged.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lola_prefill_ragged.restype = ctypes.c_int
         L.lola_decode_step.argtypes = [cp, vp, i32, vp, vp, vp, vp, vp]
         L.lola_decode_step.restype = ctypes.c_int
         L.lola_read_cache.argtypes = [cp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -130,6 +133,23 @@ def prefill(layer, state, q, k, v, out=None, workspace=None):
     _check(lib().lola_prefill_chunk(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()), "lola_prefill_chunk")
+    return out
+
+
+def prefill_ragged(layer, state, n_tokens, q, k, v, out=None, workspace=None):
+    """lola_prefill_ragged: sequence b advances by n_tokens[b] (an int32 tensor on the GPU) of the
+    k.shape[1] rows it is given; returns out [B, max_tokens, Hq, D] (rows past n_tokens[b] not written)."""
+    B, n = k.shape[0], k.shape[1]
+    if n_tokens.dtype != torch.int32 or n_tokens.numel() != B or not n_tokens.is_contiguous():
+        raise ValueError("n_tokens must be a contiguous int32 tensor of one entry per sequence")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(layer, B, n), dtype=torch.uint8, device=q.device)
+    _check(lib().lola_prefill_ragged(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(n_tokens), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream()),
+           "lola_prefill_ragged")
     return out
 
 

@@ -71,6 +71,12 @@ def test_bad_arguments_rejected_before_launch():
     assert lib.lola_prefill_chunk(ctypes.byref(cfg), None, 1, 16, p, p, p, p, p, ws, None) == -1
     assert lib.lola_prefill_chunk(ctypes.byref(cfg), p, 1, 16, mis, p, p, p, p, ws, None) == -1
     assert lib.lola_prefill_chunk(ctypes.byref(cfg), p, 1, 16, p, p, p, p, p, ws - 1, None) == -4
+    cnt, cmis = ctypes.c_void_p(8192), ctypes.c_void_p(8194)
+    assert lib.lola_prefill_ragged(ctypes.byref(cfg), p, 1, 16, None, p, p, p, p, p, ws, None) == -1
+    assert lib.lola_prefill_ragged(ctypes.byref(cfg), p, 1, 16, cmis, p, p, p, p, p, ws, None) == -1
+    assert lib.lola_prefill_ragged(ctypes.byref(cfg), p, 1, 0, cnt, p, p, p, p, p, ws, None) == -1
+    assert lib.lola_prefill_ragged(ctypes.byref(cfg), p, 1, 16, cnt, mis, p, p, p, p, ws, None) == -1
+    assert lib.lola_prefill_ragged(ctypes.byref(cfg), p, 1, 16, cnt, p, p, p, p, p, ws - 1, None) == -4
     assert lib.lola_decode_step(ctypes.byref(cfg), p, 1, None, p, p, p, None) == -1
     assert lib.lola_decode_step(ctypes.byref(cfg), p, -3, p, p, p, p, None) == -1
     assert lib.lola_init_state(ctypes.byref(cfg), 1, None, p, None) == -1

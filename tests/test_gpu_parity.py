@@ -326,3 +326,79 @@ def test_cfg5_long_context_sampled():
     for key in ("count", "pos", "k", "v", "H", "s", "tokens_seen"):
         assert torch.equal(r1[key], r2[key]), key
     print(f"cfg5: worst sampled output rel err {worst:.3g}, near ties adopted {st.forced_count}", flush=True)
+
+
+RAGGED = [
+    ("bf16_split", I.LayerConfig(8, 2, 128, 64, 16, 24, 32, "bf16"), True),
+    ("bf16_one_block", I.LayerConfig(8, 2, 128, 64, 16, 24, 32, "bf16"), False),
+    ("f32", I.LayerConfig(4, 2, 64, 32, 16, 16, 16, "f32"), True),
+]
+
+
+@pytest.mark.parametrize("name,layer,split", RAGGED, ids=[r[0] for r in RAGGED])
+def test_ragged_mixed_batch(name, layer, split, monkeypatch):
+    """lola_prefill_ragged: in one call each sequence advances by its own count (a
+    prefill chunk, one token, none).  Bitwise equal to lola_prefill_chunk on each
+    sequence alone; within tolerance of the oracle (selection rule per interval);
+    rows past a sequence's count are not written; 0 tokens leaves a sequence as is."""
+    from tests.gpu_harness import check_selection
+    if not split:
+        monkeypatch.setenv("LOLA_SCAN_SPLIT", "0")
+    L, B, C = layer.chunk, 3, layer.cache_cap
+    rounds = [[L, 1, 0], [7, L, 1], [0, 5, L], [L, L, L], [1, 0, L - 3], [3 * L + 5, 2 * L, 0]]
+    total = [sum(r[b] for r in rounds) for b in range(B)]
+    W, Q, K, V = I.random_case(900 + len(name), layer, B, max(total))
+    Wd = torch.from_numpy(W).to("cuda")
+    rag = lola.init_state(layer, B, Wd)
+    singles = [lola.init_state(layer, 1, Wd) for _ in range(B)]
+    orcs = [oracle.Oracle(layer, 1, W) for _ in range(B)]
+    tol = tol_for(layer)
+    at = [0] * B
+    for ri, counts in enumerate(rounds):
+        m = max(counts)
+        seg = [(Q[b, at[b]:at[b] + counts[b]], K[b, at[b]:at[b] + counts[b]], V[b, at[b]:at[b] + counts[b]])
+               for b in range(B)]
+
+        def padded(i):
+            X = (Q, K, V)[i]
+            P = np.zeros((B, m) + X.shape[2:], np.float32)
+            for b in range(B):
+                P[b, :counts[b]] = seg[b][i]
+            return dev(P, layer)
+
+        print(f"{name} round {ri}: counts {counts}", flush=True)
+        n_dev = torch.tensor(counts, dtype=torch.int32, device="cuda")
+        out = dev(np.full((B, m, layer.n_q_heads, layer.head_dim), 7.0, np.float32), layer)
+        lola.prefill_ragged(layer, rag, n_dev, padded(0), padded(1), padded(2), out=out)
+        rc = lola.read_cache(layer, rag, B, want_kv=False, want_state=False)
+        for b in range(B):
+            n = counts[b]
+            assert bool(torch.all(out[b, n:] == 7.0)), f"round {ri}: rows past {n} of sequence {b} written"
+            if n == 0:
+                continue
+            o1 = lola.prefill(layer, singles[b], dev(seg[b][0][None], layer), dev(seg[b][1][None], layer),
+                              dev(seg[b][2][None], layer))
+            assert torch.equal(out[b, :n], o1[0]), f"round {ri}: sequence {b} differs from its own call"
+            if m > L:
+                continue  # several intervals in one call: no per-interval cache sets to check against
+            forced = np.full((1, layer.n_kv_heads, 1, max(C, 1)), -1, np.int64)
+            sets = []
+            for g in range(layer.n_kv_heads):
+                s = [int(p) for p in rc["pos"][b, g, : int(rc["count"][b, g])].cpu().numpy()] if C > 0 else []
+                forced[0, g, 0, : len(s)] = s
+                sets.append(s)
+            ref, log = orcs[b].run(seg[b][0][None], seg[b][1][None], seg[b][2][None], log=True,
+                                   forced=forced if C > 0 else None)
+            for g in range(layer.n_kv_heads):
+                ok, _, txt = check_selection(log, 0, g, 0, sets[g], C)
+                assert ok, f"round {ri} chain ({b},{g}): {txt}"
+            err = row_rel_err(host(out[b:b + 1, :n]), ref)
+            assert err <= tol, f"round {ri} sequence {b}: output rel err {err:.3g}"
+        at = [at[b] + counts[b] for b in range(B)]
+    assert lola.check_state(layer, rag, B) == 0
+    ra = lola.read_cache(layer, rag, B)
+    assert ra["tokens_seen"].cpu().tolist() == total
+    for b in range(B):
+        rb = lola.read_cache(layer, singles[b], 1)
+        for key in ("count", "pos", "k", "v", "H", "s", "tokens_seen"):
+            assert torch.equal(ra[key][b:b + 1], rb[key]), f"sequence {b}: {key} differs from its own calls"
