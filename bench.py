@@ -213,6 +213,7 @@ def bench_decode(wl, steps_timed, warmup):
     ms = e0.elapsed_time(e1)
     us_step = 1000.0 * ms / steps_timed
     nbytes = decode_bytes(L, B)
+    mixed = bench_mixed(wl, state)
     return {
         "workload": wl.name,
         "value": B * steps_timed / (ms / 1000.0),
@@ -221,7 +222,33 @@ def bench_decode(wl, steps_timed, warmup):
         "roofline": {"bound": "hbm", "achieved": nbytes / (us_step * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": nbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
                      "bytes_per_launch": nbytes, "traffic": measured_traffic("decode")},
+        "mixed": mixed,
     }
+
+
+def bench_mixed(wl, state, steps=8, chunk_tokens=64, n_prefill=8):
+    """Continuous batching on the decode workload's states: each lola_prefill_ragged call
+    advances n_prefill sequences by a chunk and every other sequence by one token."""
+    L = wl.layer
+    B = wl.batch
+    counts, q, k, v = I.make_mixed_steps(wl, steps + 1, chunk_tokens, n_prefill)
+    cd = torch.from_numpy(counts).to("cuda")
+    q, k, v = to_dev(q, L), to_dev(k, L), to_dev(v, L)
+    out = torch.empty_like(q[0])
+    ws = torch.empty(lola.workspace_bytes(L, B, chunk_tokens), dtype=torch.uint8, device="cuda")
+    lola.prefill_ragged(L, state, cd[0], q[0], k[0], v[0], out=out, workspace=ws)  # warm-up step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(1, steps + 1):
+        lola.prefill_ragged(L, state, cd[s], q[s], k[s], v[s], out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tokens = int(counts[1:].sum())
+    return {"workload": f"{wl.name}-mixed-{n_prefill}x{chunk_tokens}+{B - n_prefill}x1",
+            "value": tokens / (ms / 1000.0), "unit": "tokens/s", "us_per_step": 1000.0 * ms / steps,
+            "tokens_per_step": tokens // steps, "steps": steps}
 
 
 def cpu_baseline(wl):

@@ -21,8 +21,9 @@ Random stream: numpy Generator(PCG64(1000*cfg + b)) for sequence b.  The
 generator of sequence 0 first draws the feature-map weights W (feat_half x D,
 entries N(0, 1/D)), then every sequence draws Q [T,Hq,D], K [T,Hkv,D],
 V [T,Hkv,D] in that order.  Decode steps (cfg 4) use a second stream
-PCG64(1000*cfg + 500 + b) per sequence, drawing q/k/v per step.  "N(0, x)"
-means variance x.
+PCG64(1000*cfg + 500 + b) per sequence, drawing q/k/v per step; the mixed
+(continuous-batching) steps over the cfg 4 sequences use PCG64(1000*cfg + 700).
+"N(0, x)" means variance x.
 """
 from __future__ import annotations
 
@@ -185,6 +186,30 @@ def make_decode_steps(wl: Workload, steps: int, batch: int | None = None):
             v[s, b] = rng.standard_normal((L.n_kv_heads, L.head_dim), dtype=np.float32)
     io = L.io_dtype
     return to_storage(q, io), to_storage(k, io), to_storage(v, io)
+
+
+def make_mixed_steps(wl: Workload, steps: int, chunk_tokens: int, n_prefill: int):
+    """Mixed (continuous-batching) steps over the decode workload's sequences: in step s,
+    sequences (s * n_prefill + j) mod B for j < n_prefill advance by a chunk of
+    `chunk_tokens` tokens, every other sequence by one token.  Returns int32 counts [S,B]
+    and N(0,1) q [S,B,chunk,Hq,D], k, v [S,B,chunk,Hkv,D], zero past each count."""
+    L = wl.layer
+    B = wl.batch
+    counts = np.ones((steps, B), np.int32)
+    q = np.zeros((steps, B, chunk_tokens, L.n_q_heads, L.head_dim), np.float32)
+    k = np.zeros((steps, B, chunk_tokens, L.n_kv_heads, L.head_dim), np.float32)
+    v = np.zeros_like(k)
+    rng = np.random.Generator(np.random.PCG64(1000 * wl.cfg_id + 700))
+    for s in range(steps):
+        for j in range(n_prefill):
+            counts[s, (s * n_prefill + j) % B] = chunk_tokens
+        for b in range(B):
+            n = int(counts[s, b])
+            q[s, b, :n] = rng.standard_normal((n, L.n_q_heads, L.head_dim), dtype=np.float32)
+            k[s, b, :n] = rng.standard_normal((n, L.n_kv_heads, L.head_dim), dtype=np.float32)
+            v[s, b, :n] = rng.standard_normal((n, L.n_kv_heads, L.head_dim), dtype=np.float32)
+    io = L.io_dtype
+    return counts, to_storage(q, io), to_storage(k, io), to_storage(v, io)
 
 
 def random_case(seed: int, layer: LayerConfig, batch: int, T: int):
