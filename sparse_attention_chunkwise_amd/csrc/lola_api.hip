@@ -210,9 +210,34 @@ Args base_args(const Dims& d, int B, void* state)
     return a;
 }
 
+// one prefill call: seqn = per-sequence token counts on the device, or null (n_tokens for all)
 lola_status prefill_impl(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens, const int32_t* seqn,
                          const void* q, const void* k, const void* v, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* events);
+                         size_t workspace_bytes, void* stream, void* const* events)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (n_tokens < 1) return LOLA_ERR_INVALID_ARG;
+    if (!state || !q || !k || !v || !out || !workspace) return LOLA_ERR_INVALID_ARG;
+    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(workspace))
+        return LOLA_ERR_INVALID_ARG;
+    Args a = base_args(d, batch, state);
+    a.n = n_tokens;
+    a.wl = ws_layout(d, batch, n_tokens);
+    a.NI = a.wl.NI;
+    if (workspace_bytes < a.wl.total) return LOLA_ERR_WORKSPACE;
+    if ((int64_t)a.NI * ((d.G * d.L + 63) / 64) > 0x7fffffff) return LOLA_ERR_UNSUPPORTED;  // grid x
+    a.ws = (unsigned char*)workspace;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.seqn = seqn;
+    return dispatch_prefill(a, (hipStream_t)stream, events);
+}
 
 }  // namespace
 
@@ -270,41 +295,6 @@ lola_status lola_prefill_ragged(const lola_config* cfg, void* state, int32_t bat
                         nullptr);
 }
 
-}  // extern "C"
-
-namespace {
-
-lola_status prefill_impl(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens, const int32_t* seqn,
-                         const void* q, const void* k, const void* v, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* events)
-{
-    Dims d;
-    lola_status st = make_dims(cfg, &d);
-    if (st != LOLA_OK) return st;
-    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
-    if (n_tokens < 1) return LOLA_ERR_INVALID_ARG;
-    if (!state || !q || !k || !v || !out || !workspace) return LOLA_ERR_INVALID_ARG;
-    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        !aligned16(workspace))
-        return LOLA_ERR_INVALID_ARG;
-    Args a = base_args(d, batch, state);
-    a.n = n_tokens;
-    a.wl = ws_layout(d, batch, n_tokens);
-    a.NI = a.wl.NI;
-    if (workspace_bytes < a.wl.total) return LOLA_ERR_WORKSPACE;
-    if ((int64_t)a.NI * ((d.G * d.L + 63) / 64) > 0x7fffffff) return LOLA_ERR_UNSUPPORTED;  // grid x
-    a.ws = (unsigned char*)workspace;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.out = out;
-    a.seqn = seqn;
-    return dispatch_prefill(a, (hipStream_t)stream, events);
-}
-
-}  // namespace
-
-extern "C" {
 
 lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch, const void* q, const void* k,
                              const void* v, void* out, void* stream)
