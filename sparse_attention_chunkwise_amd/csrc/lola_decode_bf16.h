@@ -11,12 +11,14 @@
 //             "Inferentiestrategie", step 4).
 //   manage -- the SRE equation ("Het Self-Recall Error (SRE) Mechanisme") for
 //             every cached key and the leaving key against the step-start
-//             state, computed while their keys are staged for the read:
-//             phi(k) = [softmax(W k); softmax(-W k)] by MFMA with W in three
-//             bf16 parts, n^T = H^T phi^T with H and phi in bf16 hi/lo parts,
-//             d = phi . s; then the pair with the lowest SRE (newest on a tie)
-//             is folded into H, s by one outer product when the candidates
-//             exceed the capacity, and the leaving key takes its cache slot.
+//             state: the cached keys' features come from their stored bf16
+//             hi/lo rows (written when each key entered the cache), the
+//             leaving key's are computed, phi(k) = [softmax(W k); softmax(-W k)]
+//             by MFMA with W in three bf16 parts; n^T = H^T phi^T with H and
+//             phi in bf16 hi/lo parts, d = phi . s; then the pair with the
+//             lowest SRE (newest on a tie) is folded into H, s by one outer
+//             product when the candidates exceed the capacity, and the leaving
+//             key takes its cache slot with its feature row.
 #pragma once
 
 #include <type_traits>

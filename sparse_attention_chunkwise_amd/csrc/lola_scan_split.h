@@ -1,5 +1,6 @@
-// Interval scan with each (sequence, KV head) chain spread over D/16
-// workgroups (bf16 io).
+// Interval scan with each (sequence, KV head) chain spread over D/16 x PU
+// workgroups (bf16 io): D/16 column slices of H times PU = 4, 2 or 1
+// candidate groups, as many as the device holds at once.
 //
 // The scan of one chain is a recurrence over update intervals: the SRE of the
 // cached and leaving pairs is scored against the interval-start state, the
@@ -7,9 +8,10 @@
 // sections "Het Self-Recall Error (SRE) Mechanisme" and "Inferentiestrategie").
 // With few chains (one sequence, 8 KV heads) one workgroup per chain leaves
 // most of the chip idle and puts every step of an interval on one CU.  Here
-// workgroup j of a chain owns columns [16j, 16j + 16) of H:
+// workgroup (j, u) of a chain owns columns [16j, 16j + 16) of H and the
+// candidate tiles u, u + PU, ...:
 //
-//   * its 4 waves split the candidates 16 at a time (one MFMA tile each); a
+//   * its 4 waves split those tiles (16 candidates, one MFMA tile each); a
 //     wave computes n = H^T phi(k) for its 16 columns with bf16 MFMAs on hi/lo
 //     parts (hi.hi + lo.hi + hi.lo) and d = s . phi(k) with an MFMA whose A
 //     rows are the three bf16 parts of s (d is s in fp32 times phi hi + lo),
@@ -18,15 +20,17 @@
 //     value) written and polled with agent-scope relaxed atomics, so no fence
 //     or cache flush is needed; every workgroup adds the D/16 partials in the
 //     same order and takes the same keep / fold decision;
-//   * wave 0 selects with a bisection over the SRE bit patterns held in
-//     registers (ballot counts, no LDS round trips), then compacts;
+//   * wave 0 selects with a bracketing threshold search over the SRE bit
+//     patterns held in registers (started from the previous interval's
+//     threshold, steps interpolated from the ballot counts, no LDS round
+//     trips), then compacts;
 //   * each workgroup folds the chosen pairs into its own columns only (phi hi +
 //     lo, 16 significant bits) and keeps s, which every workgroup updates
 //     identically.  Barriers inside the interval order LDS only, so global
 //     loads stay in flight across them.
 //
-// Block b runs on XCD b % 8 (round-robin dispatch), so the D/16 workgroups
-// of a chain are placed on one XCD and meet in its L2.  The launch is
+// Block b runs on XCD b % 8 (round-robin dispatch), so the workgroups of a
+// chain are placed on one XCD and meet in its L2.  The launch is
 // cooperative, so all of them are resident together; a wait that does not end
 // within a fixed number of polls marks the state as faulted and returns.
 #pragma once
