@@ -402,3 +402,53 @@ def test_ragged_mixed_batch(name, layer, split, monkeypatch):
         rb = lola.read_cache(layer, singles[b], 1)
         for key in ("count", "pos", "k", "v", "H", "s", "tokens_seen"):
             assert torch.equal(ra[key][b:b + 1], rb[key]), f"sequence {b}: {key} differs from its own calls"
+
+
+def test_ragged_mixed_batch_decode_shapes(monkeypatch):
+    """The mixed-batch launch that bench.py times: the decode workload's layer over 64
+    sequences (512 chains, past what the split scan holds at once, so the one-workgroup
+    scan runs), each prefilled with 320 tokens (window and cache full), then one
+    lola_prefill_ragged call in which sequences 8..15 take 64 tokens and the rest one.
+    Sampled sequences equal their own calls bitwise (the one-sequence states are forced
+    onto the same one-workgroup scan: the split scan folds with other rounding); two
+    follow the oracle."""
+    monkeypatch.setenv("LOLA_SCAN_SPLIT", "0")
+    wl = I.WORKLOADS[4]
+    layer, B, T0, m = wl.layer, wl.batch, 320, 64
+    W, Q, K, V = I.random_case(4242, layer, B, T0 + m)
+    Wd = torch.from_numpy(W).to("cuda")
+    rag = lola.init_state(layer, B, Wd)
+    lola.prefill(layer, rag, dev(Q[:, :T0], layer), dev(K[:, :T0], layer), dev(V[:, :T0], layer))
+    counts = np.ones(B, np.int32)
+    counts[8:16] = m
+    pad = lambda X: dev(np.where((np.arange(m)[None, :] < counts[:, None])[..., None, None], X[:, T0:T0 + m], 0.0), layer)
+    out = dev(np.full((B, m, layer.n_q_heads, layer.head_dim), 7.0, np.float32), layer)
+    lola.prefill_ragged(layer, rag, torch.from_numpy(counts).to("cuda"), pad(Q), pad(K), pad(V), out=out)
+    assert lola.check_state(layer, rag, B) == 0
+    ra = lola.read_cache(layer, rag, B)
+    C, tol = layer.cache_cap, tol_for(layer)
+    for b in (0, 9, 63):
+        n = int(counts[b])
+        print(f"mixed batch: sequence {b}, {n} tokens", flush=True)
+        assert bool(torch.all(out[b, n:] == 7.0))
+        one = lola.init_state(layer, 1, Wd)
+        lola.prefill(layer, one, dev(Q[b:b + 1, :T0], layer), dev(K[b:b + 1, :T0], layer), dev(V[b:b + 1, :T0], layer))
+        o1 = lola.prefill(layer, one, dev(Q[b:b + 1, T0:T0 + n], layer), dev(K[b:b + 1, T0:T0 + n], layer),
+                          dev(V[b:b + 1, T0:T0 + n], layer))
+        assert torch.equal(out[b, :n], o1[0]), f"sequence {b} differs from its own calls"
+        rb = lola.read_cache(layer, one, 1)
+        for key in ("count", "pos", "k", "v", "H", "s", "tokens_seen"):
+            assert torch.equal(ra[key][b:b + 1], rb[key]), f"sequence {b}: {key}"
+        if b == 63:
+            continue
+        # the oracle over the same history: the 320-token prefill as five intervals with the
+        # GPU's cache sets adopted under the margin rule, then this call's interval
+        st = Stepper(layer, 1, W)
+        for a in range(0, T0, layer.chunk):
+            st.step(Q[b:b + 1, a:a + layer.chunk], K[b:b + 1, a:a + layer.chunk], V[b:b + 1, a:a + layer.chunk])
+        g_out, r_out = st.step(Q[b:b + 1, T0:T0 + n], K[b:b + 1, T0:T0 + n], V[b:b + 1, T0:T0 + n])
+        assert torch.equal(st.last_out[0], out[b, :n]), f"sequence {b}: stepped GPU run differs"
+        err = row_rel_err(g_out, r_out)
+        assert err <= tol, f"sequence {b}: output rel err {err:.3g}"
+        eh, es = st.compare_state()
+        assert eh <= tol and es <= tol
