@@ -452,3 +452,34 @@ def test_ragged_mixed_batch_decode_shapes(monkeypatch):
         assert err <= tol, f"sequence {b}: output rel err {err:.3g}"
         eh, es = st.compare_state()
         assert eh <= tol and es <= tol
+
+
+def test_decode_full_batch_launch(monkeypatch):
+    """The decode launch that bench.py times: 64 sequences of the decode layer (512
+    workgroups, two rounds of 256 CUs), window and cache full (320-token prefill), then
+    four decode steps.  Sampled sequences equal a one-sequence run of the same history
+    bitwise (both prefilled by the one-workgroup scan, which 512 chains need), and that
+    run follows the oracle step by step."""
+    monkeypatch.setenv("LOLA_SCAN_SPLIT", "0")
+    wl = I.WORKLOADS[4]
+    layer, B, T0, steps = wl.layer, wl.batch, 320, 4
+    W, Q, K, V = I.random_case(5151, layer, B, T0 + steps)
+    Wd = torch.from_numpy(W).to("cuda")
+    full = lola.init_state(layer, B, Wd)
+    lola.prefill(layer, full, dev(Q[:, :T0], layer), dev(K[:, :T0], layer), dev(V[:, :T0], layer))
+    outs = [lola.decode(layer, full, dev(Q[:, t], layer), dev(K[:, t], layer), dev(V[:, t], layer))
+            for t in range(T0, T0 + steps)]
+    assert lola.check_state(layer, full, B) == 0
+    tol = tol_for(layer)
+    for b in (5, 62):
+        print(f"decode full batch: sequence {b}", flush=True)
+        st = Stepper(layer, 1, W)
+        for a in range(0, T0, layer.chunk):
+            st.step(Q[b:b + 1, a:a + layer.chunk], K[b:b + 1, a:a + layer.chunk], V[b:b + 1, a:a + layer.chunk])
+        for i, t in enumerate(range(T0, T0 + steps)):
+            g, r = st.step(Q[b:b + 1, t:t + 1], K[b:b + 1, t:t + 1], V[b:b + 1, t:t + 1], decode=True)
+            assert torch.equal(st.last_out[0], outs[i][b]), f"sequence {b} step {t}: differs from its own run"
+            err = row_rel_err(g, r)
+            assert err <= tol, f"sequence {b} step {t}: output rel err {err:.3g}"
+        eh, es = st.compare_state()
+        assert eh <= tol and es <= tol
