@@ -122,6 +122,7 @@ EDGE = [
     ("bf16_d64_f128", I.LayerConfig(2, 1, 64, 64, 6, 9, 10, "bf16"), 1, 55),
     ("bf16_twelve_chains", I.LayerConfig(4, 4, 64, 32, 8, 12, 16, "bf16"), 3, 90),
     ("bf16_max_interval", I.LayerConfig(2, 1, 64, 32, 16, 40, 256, "bf16"), 1, 600),
+    ("bf16_max_window", I.LayerConfig(2, 1, 64, 32, 8192, 16, 64, "bf16"), 1, 8300),
 ]
 
 
