@@ -123,6 +123,7 @@ EDGE = [
     ("bf16_twelve_chains", I.LayerConfig(4, 4, 64, 32, 8, 12, 16, "bf16"), 3, 90),
     ("bf16_max_interval", I.LayerConfig(2, 1, 64, 32, 16, 40, 256, "bf16"), 1, 600),
     ("bf16_max_window", I.LayerConfig(2, 1, 64, 32, 8192, 16, 64, "bf16"), 1, 8300),
+    ("bf16_group16", I.LayerConfig(16, 1, 64, 32, 7, 9, 11, "bf16"), 1, 50),
 ]
 
 
@@ -175,6 +176,7 @@ DECODE_EDGE = [
     ("decode_no_window", I.LayerConfig(2, 1, 64, 32, 0, 4, 8, "f32"), 1, 20, 20),
     ("decode_no_cache", I.LayerConfig(2, 2, 128, 64, 5, 0, 4, "f32"), 1, 20, 20),
     ("decode_cold_start", I.LayerConfig(4, 1, 64, 32, 8, 6, 8, "bf16"), 3, 0, 40),
+    ("decode_bf16_group16", I.LayerConfig(16, 1, 128, 64, 8, 12, 16, "bf16"), 2, 60, 20),
     ("decode_bf16_gqa", I.LayerConfig(16, 2, 128, 64, 16, 32, 16, "bf16"), 2, 100, 24),
 ]
 
