@@ -144,10 +144,15 @@ def test_edge_stepped_one_block_scan(name, layer, B, T, monkeypatch):
     _stepped(layer, B, W, Q, K, V, state_every=4, label=name + "/one-block")
 
 
+# draws whose first seed holds a sub-margin tie in some interval (the comparison
+# below would be skipped): another seed of the same shapes
+SPLIT_SEED = {"max_cache": 1200 + len("max_cache"), "bf16_twelve_chains": 1200 + len("bf16_twelve_chains")}
+
+
 @pytest.mark.parametrize("name,layer,B,T", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_split_calls(name, layer, B, T):
     """Calls of uneven sizes (each starts its own interval grid) against the oracle."""
-    W, Q, K, V = I.random_case(200 + len(name), layer, B, T)
+    W, Q, K, V = I.random_case(SPLIT_SEED.get(name, 200 + len(name)), layer, B, T)
     cuts = [max(1, T // 3), max(1, T // 5), 1]
     calls = cuts + [T - sum(cuts)]
     orc = oracle.Oracle(layer, B, W)
