@@ -70,7 +70,7 @@ def brute_outputs(layer, W, Q, K, V, cache_sets, t_start=0):
     return out
 
 
-def replay_selection(layer, W, K, V, T):
+def replay_selection(layer, W, K, V, T, choose=None):
     """Recompute every interval's candidates, scores and kept set from scratch.
 
     Candidates at interval [a, e): the cache plus positions max(0,a-w)..e-1-w.
@@ -78,7 +78,11 @@ def replay_selection(layer, W, K, V, T):
     rebuilt from the folded set (not updated in place).  Scores: the
     Nadaraya-Watson form of the SRE, r = sum_f kappa_f v_f / sum_f kappa_f
     with kappa_f = phi(k).phi(k_f) (0 when nothing is folded).
-    Returns per chain a list of dicts (cand positions, scores, kept set).
+    choose(b, g, c, U, scores, own) may replace the kept set `own` (the first
+    min(C, |U|) by score descending, position ascending) by another list of
+    positions; the rest of the candidates are folded.
+    Returns per chain a list of dicts (cand positions, scores, own and kept
+    sets) and, per chain, the folded positions in fold order.
     """
     w, C, L = layer.window, layer.cache_cap, layer.chunk
     B = K.shape[0]
@@ -100,12 +104,15 @@ def replay_selection(layer, W, K, V, T):
                     r = np.zeros((len(U), Vg.shape[1]))
                 sc = ((r - Vg[U]) ** 2).sum(axis=1) if U else np.zeros(0)
                 order = sorted(range(len(U)), key=lambda i: (-sc[i], U[i]))
-                keep = [U[i] for i in order[: min(C, len(U))]]
-                gone = [U[i] for i in order[min(C, len(U)):]]
-                steps.append({"U": U, "sre": sc, "keep": set(keep), "order": order})
+                own = [U[i] for i in order[: min(C, len(U))]]
+                keep = own if choose is None else list(choose(b, g, len(steps), U, sc, own))
+                gone = [u for u in U if u not in set(keep)]
+                steps.append({"U": U, "sre": sc, "keep": set(keep), "own": set(own), "order": order,
+                              "folded": list(folded)})
                 folded.extend(gone)
                 S = keep
-            per_b.append(steps)
+            steps_final = {"folded": folded}
+            per_b.append(steps + [steps_final])
         res.append(per_b)
     return res
 
@@ -271,7 +278,7 @@ def check_selection_replay(lib, layer=None, T=None, B=1, seed=7, keys=None):
         rep = replay_selection(lay, W, K, V, TT)
         for b in range(B):
             for g in range(lay.n_kv_heads):
-                for c, st in enumerate(rep[b][g]):
+                for c, st in enumerate(rep[b][g][:-1]):
                     nU = int(log["n_cand"][b, g, c])
                     pos = [int(p) for p in log["cand_pos"][b, g, c, :nU]]
                     assert sorted(pos) == sorted(st["U"]), (b, g, c, pos, st["U"])
@@ -280,6 +287,96 @@ def check_selection_replay(lib, layer=None, T=None, B=1, seed=7, keys=None):
                         assert abs(got[u] - e) <= 1e-9 * max(1.0, abs(e)), (u, got[u], e)
                     kept = set(int(p) for p in log["own_kept"][b, g, c] if p >= 0) if lay.cache_cap else set()
                     assert kept == st["keep"], (b, g, c, kept, st["keep"])
+
+
+def check_forced_selection(lib):
+    """Teacher forcing: the oracle adopts a kept set given from outside.
+
+    Several chains (2 sequences x 2 KV heads, which share candidate positions)
+    run many intervals in one call; in a third of the intervals, with an offset
+    that differs per chain, the kept set is a seeded random valid choice instead
+    of the top C.  The candidates and scores the oracle logs, the outputs, and
+    the final H, s must equal an independent replay that makes the same choices
+    (outputs through the per-key-weight brute force with those cache sets), and
+    the oracle must still log its own top-C choice.  Invalid forced sets (a
+    position that is not a candidate, a repeated position, too few positions)
+    are rejected."""
+    layer = LayerConfig(2, 2, 8, 3, 3, 3, 4, "f32")
+    B, T, C, Hkv = 2, 37, layer.cache_cap, layer.n_kv_heads
+    NI = (T + layer.chunk - 1) // layer.chunk
+    W, Q, K, V = _case(layer, T, B=B, seed=13)
+    rng = np.random.default_rng(14)
+    differs = []
+
+    def choose(b, g, c, U, sc, own):
+        if len(U) > C and (c + b + 2 * g) % 3 == 0:
+            pick = sorted(int(x) for x in rng.choice(U, size=C, replace=False))
+            differs.append(set(pick) != set(own))
+            return pick
+        return own
+
+    rep = replay_selection(layer, W, K, V, T, choose=choose)
+    assert sum(differs) >= 4, "the forcing changed too few intervals to test anything"
+    forced = np.full((B, Hkv, NI, C), -1, np.int64)
+    sets = []
+    for b in range(B):
+        per_b = []
+        for g in range(Hkv):
+            seq = [set()]
+            for c in range(NI):
+                kp = sorted(rep[b][g][c]["keep"])
+                forced[b, g, c, :len(kp)] = kp
+                seq.append(set(kp))
+            per_b.append(seq)
+        sets.append(per_b)
+    # forced sets of different chains and intervals differ: a wrong offset cannot pass
+    assert any(set(forced[0, 0, c]) != set(forced[0, 1, c]) for c in range(NI))
+    assert any(set(forced[0, 0, c]) != set(forced[1, 0, c]) for c in range(NI))
+    orc = oracle.Oracle(layer, B, W, lib)
+    o, log = orc.run(Q, K, V, forced=forced, log=True)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(NI):
+                st = rep[b][g][c]
+                nU = int(log["n_cand"][b, g, c])
+                pos = [int(p) for p in log["cand_pos"][b, g, c, :nU]]
+                assert sorted(pos) == sorted(st["U"]), (b, g, c)
+                got = dict(zip(pos, log["cand_sre"][b, g, c, :nU]))
+                for u, e in zip(st["U"], st["sre"]):
+                    assert abs(got[u] - e) <= 1e-9 * max(1.0, abs(e)), (b, g, c, u)
+                own = set(int(p) for p in log["own_kept"][b, g, c] if p >= 0)
+                assert own == st["own"], (b, g, c)
+            ch = orc.chain(b, g)
+            folded = rep[b][g][-1]["folded"]
+            pk = phi_rows(W[g], K[b, folded, g])
+            np.testing.assert_allclose(ch["H"], pk.T @ V[b, folded, g], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(ch["s"], pk.sum(0), rtol=1e-11, atol=1e-12)
+            assert sorted(ch["cache_pos"].tolist()) == sorted(rep[b][g][NI - 1]["keep"])
+    ref = brute_outputs(layer, W, Q, K, V, sets)
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+    # invalid forced sets
+    _, lg0 = oracle.Oracle(layer, B, W, lib).run(None, K[:, :12], V[:, :12], want_out=False, log=True)
+    c_full = next(c for c in range(3) if int(lg0["n_cand"][0, 0, c]) > C)
+    base = np.full((B, Hkv, 3, C), -1, np.int64)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(3):
+                kp = [int(p) for p in lg0["own_kept"][b, g, c] if p >= 0]
+                base[b, g, c, :len(kp)] = kp
+    oracle.Oracle(layer, B, W, lib).run(None, K[:, :12], V[:, :12], want_out=False, forced=base)
+    for bad in ("not_a_candidate", "repeated", "too_few"):
+        f = base.copy()
+        if bad == "not_a_candidate":
+            f[1, 1, c_full, 0] = T + 5
+        elif bad == "repeated":
+            f[1, 1, c_full, 1] = f[1, 1, c_full, 0]
+        else:
+            f[1, 1, c_full, C - 1] = -1
+        try:
+            oracle.Oracle(layer, B, W, lib).run(None, K[:, :12], V[:, :12], want_out=False, forced=f)
+        except ValueError:
+            continue
+        raise AssertionError(f"forced set with a {bad} entry accepted")
 
 
 def check_conservation(lib):
@@ -408,6 +505,7 @@ ALL_CHECKS = [
     check_no_cache_independent_of_interval,
     check_per_key_weights,
     check_selection_replay,
+    check_forced_selection,
     check_conservation,
     check_kept_outrank_folded,
     check_tie_order,

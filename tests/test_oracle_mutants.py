@@ -31,6 +31,14 @@ MUTANTS = {
     "window_keeps_one_less": [("if (Rpos[i] < e - w) continue;", "if (Rpos[i] < e - w + 1) continue;")],
     "fold_transposed_value": [("c->H[(size_t)i * D + j] += ph[i] * Uv[u][j];",
                                "c->H[(size_t)i * D + j] += ph[i] * Uv[u][D - 1 - j];")],
+    # teacher forcing (a kept set adopted from outside)
+    "forced_set_of_wrong_head": [("jb->forced + (((size_t)b * Hkv + g) * jb->NI + ci)",
+                                  "jb->forced + (((size_t)b * Hkv + 0) * jb->NI + ci)")],
+    "forced_set_of_first_interval": [("jb->forced + (((size_t)b * Hkv + g) * jb->NI + ci)",
+                                      "jb->forced + (((size_t)b * Hkv + g) * jb->NI + 0)")],
+    "forced_kept_pair_also_folded": [("        if (keep[u]) continue;\n        const double* ph = Uphi",
+                                      "        if (keep[u] && !(jb->forced && u == 0)) continue;\n"
+                                      "        const double* ph = Uphi")],
 }
 
 
