@@ -40,6 +40,17 @@
  *     bf16; H, s and W are always fp32.
  *   - Errors are returned as lola_status before anything is enqueued;
  *     a failed HIP launch returns LOLA_ERR_HIP.  Nothing aborts or prints.
+ *   - The state header (magic, format version, a hash of the config and the
+ *     batch, a fault word) is also tested on the device, by every kernel
+ *     before it touches anything else: a state initialised for another
+ *     config or batch, or one that an earlier call marked faulted, is left
+ *     unchanged by lola_prefill_chunk, lola_prefill_ragged and
+ *     lola_decode_step (no state byte, output row or workspace byte is
+ *     written) although the call itself returns LOLA_OK, since the host
+ *     never waits for the device.  lola_check_state reports such a state as
+ *     LOLA_ERR_BAD_STATE.  Only the first 32 bytes of the buffer are read
+ *     for the test, so a buffer sized for another config is never read or
+ *     written past them.
  *   - One state buffer must not be used by two calls at once (on any
  *     streams); distinct state buffers are independent.
  *   - Supported shapes: head_dim 64 or 128; feat_half 32 or 64;
@@ -79,10 +90,13 @@ typedef struct {
     float softmax_scale;   /* tau on q.k; <= 0 selects 1/sqrt(head_dim) */
 } lola_config;
 
-/* Bytes of the state buffer for `batch` sequences (header, tokens seen, W,
- * and per (sequence, KV head): H [F][D] f32, s [F] f32, cache positions,
- * window ring and cache keys/values, and for bf16 io the feature rows of the
- * cached keys).  0 if the config is not supported. */
+/* Bytes of the state buffer for `batch` sequences: a header, W, and per
+ * (sequence, KV head) the three memories of the summary's "Methodologie:
+ * LoLA" section -- the sliding window (ring of the last `window` keys and
+ * values), the sparse cache (positions, keys, values, and for bf16 io the
+ * feature rows of the cached keys) and the recurrent state H [F][D] f32,
+ * s [F] f32 -- plus the tokens seen.  The size does not grow with the
+ * sequence length.  0 if the config or batch is not supported. */
 size_t lola_state_bytes(const lola_config* cfg, int32_t batch);
 
 /* Bytes of scratch that lola_prefill_chunk needs for up to `max_tokens`
@@ -91,17 +105,28 @@ size_t lola_state_bytes(const lola_config* cfg, int32_t batch);
 size_t lola_prefill_workspace_bytes(const lola_config* cfg, int32_t batch, int32_t max_tokens);
 
 /* Initialise `state` (device, lola_state_bytes) for `batch` empty sequences:
- * header, tokens seen = 0, H = 0, s = 0, empty cache and window.
- * W: device [n_kv_heads][feat_half][head_dim] f32, copied into the state. */
+ * header, tokens seen = 0, H = 0, s = 0, empty cache and window -- the three
+ * memories of "Methodologie: LoLA" before any pair has been seen.
+ * W: device [n_kv_heads][feat_half][head_dim] f32, copied into the state; it
+ * defines the feature map phi(x) = [softmax(W x); softmax(-W x)] (the paper
+ * abstract only calls it a low-rank feature map; this form is the
+ * library's).  Errors: LOLA_ERR_INVALID_ARG for a NULL or misaligned W or
+ * state, LOLA_ERR_UNSUPPORTED for a config outside the supported set. */
 lola_status lola_init_state(const lola_config* cfg, int32_t batch, const float* W, void* state,
                             void* stream);
 
-/* Advance every sequence by n_tokens (> 0) tokens: positions
+/* Advance every sequence by n_tokens (> 0) tokens in the chunkwise mode of
+ * the summary's "Inferentiestrategie" section: positions
  * [t0, t0 + n_tokens) are processed as consecutive update intervals of
  * cfg->chunk tokens (the last may be shorter), each call starting its own
  * interval grid at t0.  Per interval: outputs of its queries from the
- * interval-start memories, then SRE scoring of leaving + cached pairs, top-C
- * keep, fold of the rest, window update.
+ * interval-start memories (step 4), then SRE scoring of leaving + cached
+ * pairs (step 1), top-C keep (step 2), fold of the rest (step 3), window
+ * update.
+ * Errors (host side, before any launch): LOLA_ERR_INVALID_ARG for NULL or
+ * misaligned pointers or n_tokens < 1, LOLA_ERR_UNSUPPORTED for a config or
+ * batch outside the supported set, LOLA_ERR_WORKSPACE for a short workspace,
+ * LOLA_ERR_HIP for a failed launch; device side, see the state header above.
  *   q   [batch][n_tokens][n_q_heads][head_dim]  io dtype
  *   k,v [batch][n_tokens][n_kv_heads][head_dim] io dtype
  *   out [batch][n_tokens][n_q_heads][head_dim]  io dtype (written)
@@ -141,16 +166,26 @@ lola_status lola_prefill_ragged(const lola_config* cfg, void* state, int32_t bat
                                 const int32_t* n_tokens, const void* q, const void* k, const void* v,
                                 void* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* One token for every sequence: identical in result to
- * lola_prefill_chunk(n_tokens = 1) (a one-token interval), in one fused launch
- * that needs no workspace.
+/* One token for every sequence: the token-by-token mode of the summary's
+ * "Inferentiestrategie" section (its steps 1-4 on a one-token interval), in
+ * one fused launch that needs no workspace.  It computes what
+ * lola_prefill_chunk(n_tokens = 1) computes and keeps the same pair (SRE
+ * descending, position ascending); the arithmetic differs (the fold of the
+ * one evicted pair runs in fp32 vector FMAs instead of MFMAs, the softmax in
+ * other blocks), so outputs and H, s agree within the io dtype's tolerance
+ * rather than bit for bit.
  *   q [batch][n_q_heads][head_dim], k, v [batch][n_kv_heads][head_dim],
- *   out [batch][n_q_heads][head_dim], all io dtype. */
+ *   out [batch][n_q_heads][head_dim], all io dtype.
+ * Errors: as lola_prefill_chunk (no workspace). */
 lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch, const void* q,
                              const void* k, const void* v, void* out, void* stream);
 
 /* Copy the memories out of `state` into caller device buffers (any output
- * may be NULL).  Cache entries are written in ascending position order.
+ * may be NULL): the sparse cache and the recurrent state H, s of
+ * "Methodologie: LoLA", e.g. to inspect which pairs the SRE kept
+ * ("Inferentiestrategie", step 2).  Cache entries are written in ascending
+ * position order.  A state whose header does not match the config and batch
+ * leaves every output unwritten (a faulted state is still read).
  *   count [batch][n_kv_heads] int32       entries held
  *   pos   [batch][n_kv_heads][cache_cap]  int64, ascending, -1 padded
  *   k_out, v_out [batch][n_kv_heads][cache_cap][head_dim] io dtype, 0 padded

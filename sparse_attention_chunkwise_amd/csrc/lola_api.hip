@@ -199,12 +199,13 @@ lola_status launch_decode(Args& a, hipStream_t s)
 lola_status dispatch_prefill(Args& a, hipStream_t s, void* const* ev) { LOLA_DISPATCH(launch_prefill, a, s, ev); }
 lola_status dispatch_decode(Args& a, hipStream_t s) { LOLA_DISPATCH(launch_decode, a, s); }
 
-Args base_args(const Dims& d, int B, void* state)
+Args base_args(const lola_config* cfg, const Dims& d, int B, void* state)
 {
     Args a;
     memset(&a, 0, sizeof(a));
     a.d = d;
     a.B = B;
+    a.hash = cfg_hash(cfg, B);
     a.state = (unsigned char*)state;
     a.sl = state_layout(d, B);
     return a;
@@ -224,7 +225,7 @@ lola_status prefill_impl(const lola_config* cfg, void* state, int32_t batch, int
     if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         !aligned16(workspace))
         return LOLA_ERR_INVALID_ARG;
-    Args a = base_args(d, batch, state);
+    Args a = base_args(cfg, d, batch, state);
     a.n = n_tokens;
     a.wl = ws_layout(d, batch, n_tokens);
     a.NI = a.wl.NI;
@@ -264,7 +265,7 @@ lola_status lola_init_state(const lola_config* cfg, int32_t batch, const float* 
     if (st != LOLA_OK) return st;
     if ((st = check_batch(batch, d)) != LOLA_OK) return st;
     if (!W || !state || !aligned16(W) || !aligned16(state)) return LOLA_ERR_INVALID_ARG;
-    Args a = base_args(d, batch, state);
+    Args a = base_args(cfg, d, batch, state);
     hipLaunchKernelGGL(init_kernel, dim3(batch * d.Hkv + 1), dim3(256), 0, (hipStream_t)stream, a, W,
                        cfg_hash(cfg, batch));
     return hip_status(hipGetLastError());
@@ -306,7 +307,7 @@ lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch,
     if (!state || !q || !k || !v || !out) return LOLA_ERR_INVALID_ARG;
     if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LOLA_ERR_INVALID_ARG;
-    Args a = base_args(d, batch, state);
+    Args a = base_args(cfg, d, batch, state);
     a.n = 1;
     a.NI = 1;
     a.q = q;
@@ -327,7 +328,7 @@ lola_status lola_read_cache(const lola_config* cfg, const void* state, int32_t b
     const void* outs[] = {count, pos, k_out, v_out, H_out, s_out, tokens_seen};
     for (const void* p : outs)
         if (p && ((uintptr_t)p & 7u)) return LOLA_ERR_INVALID_ARG;
-    Args a = base_args(d, batch, const_cast<void*>(state));
+    Args a = base_args(cfg, d, batch, const_cast<void*>(state));
     hipStream_t s = (hipStream_t)stream;
     if (d.io == LOLA_F32)
         hipLaunchKernelGGL(read_cache_kernel<float>, dim3(batch * d.Hkv), dim3(256), 0, s, a, count, pos,

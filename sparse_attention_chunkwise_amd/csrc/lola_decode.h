@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a)
 {
     constexpr int NW = 4, HP = D + 4, Fh = F / 2, NH = F / 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const Dims& d = a.d;
     const int G = d.G, w = d.w, C = d.C;
     const DecodeSmem sm = decode_smem(D, F, G, C);

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     constexpr int KBL = kDecBlock, KW = KBL / NW;  // keys per block, per wave
     constexpr int HP = F + 8, VP = KBL + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const Dims& d = a.d;
     const int G = d.G, w = d.w, C = d.C;
     const DecSmem sm = dec_smem<D, F>(C);  // only the last two offsets depend on C

@@ -69,6 +69,7 @@ struct StateHeader {
     int32_t fault;  // nonzero once a prefill scan gave up waiting for a sibling workgroup
     int32_t pad[2];
 };
+static_assert(sizeof(StateHeader) == 32, "kernels test the first 32 bytes of a state");
 
 // State buffer: header | W [Hkv][Fh][D] f32 | Wb [Hkv][3][Fh][D] bf16 (three parts of W, largest first) | chains [B][Hkv]
 // chain: tokens seen i64 | cache_count i32 | H^T [D][F] f32 | s [F] f32 | cache_pos [C] i32 |
@@ -116,7 +117,7 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 //   cache0_k/v [B][Hkv][C][D] io | cphi [B][Hkv][C][F] f32 |
 //   phiS [B][Hkv][X][2F] bf16 | cphiS [B][Hkv][C][2F] bf16 (hi then lo parts of
 //   phi, features in the SRE operand order) |
-//   snapH [B][Hkv][NI][D][F] H^T: f32 for f32 io; bf16 in operand order for bf16 io |
+//   snapH [B][Hkv][NI][D][F] H^T: f32 for f32 io; bf16 (hi part) in operand order for bf16 io |
 //   snapS [B][Hkv][NI][F] f32 |
 //   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32 |
 //   xsync [B][Hkv][16] u32 (give-up flag, reads-done counter) |
@@ -145,7 +146,7 @@ inline __host__ __device__ WsLayout ws_layout(const Dims& d, int B, int n)
     s.cphi = off;     off = align_up(off + sizeof(float) * ch * Cp * d.F, 256);
     s.phiS = off;     off = align_up(off + sizeof(uint16_t) * ch * s.X * 2 * d.F, 256);
     s.cphiS = off;    off = align_up(off + sizeof(uint16_t) * ch * Cp * 2 * d.F, 256);
-    s.snapH = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F * d.D, 256);
+    s.snapH = off;    off = align_up(off + (size_t)(d.io == 1 ? 2 : 4) * ch * s.NI * d.F * d.D, 256);
     s.snapS = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F, 256);
     s.snapRef = off;  off = align_up(off + sizeof(int32_t) * ch * s.NI * Cp, 256);
     s.snapN = off;    off = align_up(off + sizeof(int32_t) * ch * s.NI, 256);
@@ -239,6 +240,7 @@ __device__ __forceinline__ float wave_sum(float v)
 struct Args {
     Dims d;
     int B, n, NI;           // n: rows per sequence in q, k, v, out; NI: intervals of n tokens
+    uint64_t hash;          // configuration hash the state header must carry
     const int32_t* seqn;    // device [B]: tokens of each sequence (<= n), or null: n for all
     unsigned char* state;
     unsigned char* ws;
@@ -249,6 +251,20 @@ struct Args {
     StateLayout sl;
     WsLayout wl;
 };
+
+// The state header was written by lola_init_state for this configuration and
+// batch, and no earlier call marked the state faulted.  Kernels that advance or
+// read a state test this first and, if it fails, return without writing anything,
+// so a state meant for another configuration is never read or written with this
+// one's layout.  (The fields are read with uniform addresses, so every wave of a
+// workgroup takes the same branch as long as no other workgroup of the same launch
+// writes the header; only the split scan does, and it broadcasts its test.)
+__device__ __forceinline__ bool state_ok(const Args& a, bool allow_faulted = false)
+{
+    const StateHeader* h = (const StateHeader*)a.state;
+    return h->magic == kMagic && h->version == kVersion && h->cfg_hash == a.hash && h->batch == a.B &&
+           (allow_faulted || h->fault == 0);
+}
 
 // Tokens sequence b consumes in this call: its entry of the per-sequence counts
 // clamped to [0, n], or n when the call has none.

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                   DT = D / 16;
     constexpr int KP = D + 8, VP = KB + 8, PP = F + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const Dims& d = a.d;
     constexpr OutSmem sm = out_smem<D, F>(1);  // every offset used here is independent of C
     float* sP = (float*)(smem + sm.sP);

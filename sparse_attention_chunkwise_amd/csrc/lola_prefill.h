@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
     constexpr int RPW = 16;  // rows per wave
     __shared__ float Ws[Fh][D + 1];
     __shared__ float xs[4][D];
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int w = a.d.w, C = a.d.C, X = a.wl.X, ns = seq_tokens(a, b);
@@ -223,6 +224,7 @@ template <int D, int Fh>
 __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_rows)
 {
     constexpr int F = 2 * Fh, FTH = Fh / 16, DS = D / 32;
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const int chain = blockIdx.y, b = chain / a.d.Hkv, g = chain % a.d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
     const int w = a.d.w, C = a.d.C, X = a.wl.X, Cp = C > 0 ? C : 1, ns = seq_tokens(a, b);
@@ -461,6 +463,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const ScanSmem sm = scan_smem(D, F, C, L, sizeof(T));
     const int SPS = sm.sphi_stride, SVS = sm.sv_stride;
     uint16_t* stP = (uint16_t*)(smem + sm.stage);                   // [BATCH][SPS]
@@ -988,6 +991,7 @@ __global__ __launch_bounds__(256) void output_kernel(Args a)
     constexpr int QM = D / (4 * KPL);     // MFMAs per D contraction
     constexpr int FM = (F / 4) / KPL;     // MFMAs per F contraction
     constexpr int NH = F / 4;             // feature values held per lane
+    if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const Dims& d = a.d;
     const int G = d.G, L = d.L, w = d.w;
     const int chain = blockIdx.y, b = chain / d.Hkv, g = chain % d.Hkv;

@@ -87,6 +87,9 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     static_assert(EC * 4 == NT && EC == 64 && (2 * F / 8) % (2 * NW) == 0, "fold staging covers the chunk exactly");
     static_assert(5 * 64 <= kMaxCache && 5 * 64 <= kMaxCand, "register selection reads 5 chunks of cref and ebits");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // header fields other than `fault` are the same for every block of the launch, so
+    // a mismatch returns every block at once; `fault` is tested below, block-uniformly
+    if (!state_ok(a, true)) return;
     const Dims& d = a.d;
     const int w = d.w, C = d.C, L = d.L;
     const int chains = a.B * d.Hkv;
@@ -185,11 +188,21 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         cpos[i] = ch.cpos()[i];
         cref[i] = -(i + 1);
     }
-    if (tid == 0) misc[8] = 0;
-    lds_sync();
+    if (tid == 0) {
+        misc[8] = 0;
+        misc[9] = __hip_atomic_load(&((StateHeader*)a.state)->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // (a full barrier: it also waits until every wave's loads of H, s, the count and
+    // the positions have returned, before the count below says they are read)
+    __syncthreads();
+    // An earlier call left the state faulted: write nothing.  Every block sees that
+    // fault word (an earlier launch wrote it), so none of them waits for another; a
+    // block that sees it set by a sibling of this launch (one that gave up waiting)
+    // finds the give-up flag xsync[1] already raised for the others.
+    if (misc[9] != 0) return;
     for (int i = tid; i < F; i += NT) split3(i);
-    // block 0 rewrites s, the count and the cache positions at the end: it waits
-    // until every block of the chain has read them (counter xsync[2])
+    // the lead blocks rewrite H, and block 0 also s, the count and the cache positions,
+    // at the end: they wait until every block of the chain has read them (counter xsync[2])
     if (tid == 0) __hip_atomic_fetch_add(&xsync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     const uint16_t* phiS0 = ws_phiS(a, chain, 0);
@@ -912,16 +925,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             }
         }
     }
-    // this column slice's rows of H^T (lead blocks); block 0 also s, positions, counts
+    // this column slice's rows of H^T (lead blocks); block 0 also s, positions, counts.
+    // Every block of the chain reads H, s, the count and the positions at its start;
+    // with no exchange in a call (no cache, or no interval that must select) nothing
+    // else orders a late-starting block's reads before these stores, so each lead block
+    // first waits until all KW * PU blocks have counted their reads in xsync[2].
     if (!lead) return;
-#pragma unroll
-    for (int h = 0; h < HT; ++h) {
-        const int ft = wave + NW * h;
-        if (ft < FT)
-            *(float4*)(ch.H() + (size_t)(col0 + r16) * F + ft * 16 + qg * 4) =
-                make_float4(Hacc[h][0], Hacc[h][1], Hacc[h][2], Hacc[h][3]);
-    }
-    if (jw != 0) return;
     if (tid == 0) {
         uint32_t polls = 0;
         while (__hip_atomic_load(&xsync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)(KW * PU)) {
@@ -934,6 +943,14 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         }
     }
     lds_sync();
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+        const int ft = wave + NW * h;
+        if (ft < FT)
+            *(float4*)(ch.H() + (size_t)(col0 + r16) * F + ft * 16 + qg * 4) =
+                make_float4(Hacc[h][0], Hacc[h][1], Hacc[h][2], Hacc[h][3]);
+    }
+    if (jw != 0) return;
     for (int i = tid; i < F; i += NT) ch.s()[i] = sP[perm_pos(i)];
     for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
     if (tid == 0) {

@@ -90,7 +90,14 @@ def torch_dtype(layer):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor the C ABI reads as densely packed: a strided view
+    (a slice along a non-leading dimension, a transpose) is rejected, not copied."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("liblola takes densely packed tensors; got a strided view "
+                         f"of shape {tuple(t.shape)} (call .contiguous() first)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream():
