@@ -124,6 +124,16 @@ def to_dev(x, layer):
     return t.to(torch.bfloat16) if layer.io_dtype == "bf16" else t
 
 
+def require_healthy(layer, states, B, what):
+    """Exit non-zero if any timed state was marked faulted (a split scan that gave up
+    waiting returns early, and its shorter time must not be reported)."""
+    for st in states:
+        rc = lola.check_state(layer, st, B)
+        if rc != 0:
+            print(f"bench.py: {what}: a timed state is faulted ({lola.status_string(rc)})", file=sys.stderr)
+            sys.exit(3)
+
+
 def bench_prefill(wl, steps, warmup):
     """Time `steps` prefill launches, each from a fresh state, cold and warm.
 
@@ -172,6 +182,7 @@ def bench_prefill(wl, steps, warmup):
 
     cold = timed(0, True)
     warm = timed(steps, False)
+    require_healthy(L, states, B, "prefill")
     cold["tokens"] = B * T
     cold["warm"] = warm
     return cold
@@ -197,31 +208,52 @@ def bench_decode(wl, steps_timed, warmup):
     state = lola.init_state(L, B, Wd)
     lola.prefill(L, state, q, k, v)
     del q, k, v
+    require_healthy(L, [state], B, "decode prefill")
     qd, kd, vd = I.make_decode_steps(wl, steps_timed)
     qd, kd, vd = to_dev(qd, L), to_dev(kd, L), to_dev(vd, L)
     outd = torch.empty_like(qd[0])
-    warm = state.clone()
+    base = state.clone()
+    warm_state = state.clone()
     for s in range(warmup):
-        lola.decode(L, warm, qd[s], kd[s], vd[s], out=outd)
+        lola.decode(L, warm_state, qd[s], kd[s], vd[s], out=outd)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s in range(steps_timed):
-        lola.decode(L, state, qd[s], kd[s], vd[s], out=outd)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    us_step = 1000.0 * ms / steps_timed
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def timed(st, cold):
+        """Per-step events; cold: the 512 MiB buffer is rewritten before each step,
+        outside its events, so each step reads the state from HBM."""
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps_timed)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps_timed)]
+        for s in range(steps_timed):
+            if cold:
+                flush.fill_(s & 0xFF)
+            e0[s].record()
+            lola.decode(L, st, qd[s], kd[s], vd[s], out=outd)
+            e1[s].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1000.0
+
+    cold_state = base.clone()
+    us_cold = timed(cold_state, True)
+    us_warm = timed(state, False)
+    require_healthy(L, [cold_state, state, warm_state], B, "decode")
+    del cold_state, warm_state, base, flush
     nbytes = decode_bytes(L, B)
+
+    def roof(us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "bytes_per_launch": nbytes, "traffic": measured_traffic("decode")}
+
     mixed = bench_mixed(wl, state)
     return {
         "workload": wl.name,
-        "value": B * steps_timed / (ms / 1000.0),
+        "value": B / (us_cold * 1e-6),
         "unit": "tokens/s",
-        "us_per_step": us_step,
-        "roofline": {"bound": "hbm", "achieved": nbytes / (us_step * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": nbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                     "bytes_per_launch": nbytes, "traffic": measured_traffic("decode")},
+        "us_per_step": us_cold,
+        "timing": "cold (512 MiB rewritten before each step, outside its events), per-step HIP events",
+        "roofline": roof(us_cold),
+        "warm": {"value": B / (us_warm * 1e-6), "us_per_step": us_warm, "roofline": roof(us_warm)},
         "mixed": mixed,
     }
 
@@ -244,6 +276,7 @@ def bench_mixed(wl, state, steps=8, chunk_tokens=64, n_prefill=8):
         lola.prefill_ragged(L, state, cd[s], q[s], k[s], v[s], out=out, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
+    require_healthy(L, [state], B, "mixed batch")
     ms = e0.elapsed_time(e1)
     tokens = int(counts[1:].sum())
     return {"workload": f"{wl.name}-mixed-{n_prefill}x{chunk_tokens}+{B - n_prefill}x1",
@@ -251,19 +284,55 @@ def bench_mixed(wl, state, steps=8, chunk_tokens=64, n_prefill=8):
             "tokens_per_step": tokens // steps, "steps": steps}
 
 
-def cpu_baseline(wl):
-    """The fp64 oracle on the host cores over the same 4096-token workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, wl_dec, dec_seqs=4, dec_steps=16):
+    """The fp64 oracle on the host cores: the full 4096-token prefill workload on one thread
+    and on all the threads it can use (one per KV-head chain), and a sample of the decode
+    workload (dec_seqs of its 64 sequences: their 4096-token prefill in state-only mode,
+    untimed, then dec_steps timed decode steps)."""
     import oracle
 
+    nproc = os.cpu_count() or 1
     W, Q, K, V = I.make_batch(wl)
-    nthreads = min(os.cpu_count() or 1, wl.batch * wl.layer.n_kv_heads)
-    orc = oracle.Oracle(wl.layer, wl.batch, W)
+    nthreads = min(nproc, wl.batch * wl.layer.n_kv_heads, 16)
+    runs = {}
+    for nt in sorted({1, nthreads}):
+        orc = oracle.Oracle(wl.layer, wl.batch, W)
+        t0 = time.perf_counter()
+        orc.run(Q, K, V, nthreads=nt)
+        runs[nt] = time.perf_counter() - t0
+    # decode sample
+    L = wl_dec.layer
+    Wd, Qd, Kd, Vd = I.make_batch(wl_dec, batch=dec_seqs)
+    qd, kd, vd = I.make_decode_steps(wl_dec, dec_steps, batch=dec_seqs)
+    dthreads = min(nproc, dec_seqs * L.n_kv_heads, 16)
+    orc = oracle.Oracle(L, dec_seqs, Wd)
+    orc.run(None, Kd, Vd, want_out=False, nthreads=dthreads)
     t0 = time.perf_counter()
-    orc.run(Q, K, V, nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    return {"value": wl.batch * wl.seq_len / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"one full pass of the {wl.seq_len}-token workload (all {wl.layer.n_q_heads} query heads), "
-                      f"fp64, {nthreads} threads (one per KV-head chain), {dt:.1f} s"}
+    for s in range(dec_steps):
+        orc.run(qd[s][:, None], kd[s][:, None], vd[s][:, None], nthreads=dthreads)
+    dt_dec = time.perf_counter() - t0
+    tok = wl.batch * wl.seq_len
+    return {"value": tok / runs[nthreads], "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"one full pass of the {wl.seq_len}-token prefill workload (all {wl.layer.n_q_heads} query "
+                      f"heads, outputs and state), fp64, {nthreads} threads (one per KV-head chain): "
+                      f"{runs[nthreads]:.1f} s",
+            "single_thread": {"value": tok / runs[1], "unit": "tokens/s", "cores": 1, "seconds": runs[1]},
+            "nproc": nproc, "cpu_model": cpu_model(),
+            "decode": {"workload": wl_dec.name, "value": dec_seqs * dec_steps / dt_dec, "unit": "tokens/s",
+                       "cores": dthreads, "us_per_step": 1e6 * dt_dec / dec_steps,
+                       "sample": f"{dec_seqs} of the {wl_dec.batch} sequences (state-only 4096-token prefill, "
+                                 f"untimed), {dec_steps} timed decode steps with outputs, {dthreads} threads"}}
 
 
 def bench_long(steps=3):
@@ -351,7 +420,8 @@ def main():
                          "gbs": work[name]["bytes"] / (us * 1e-6) / 1e9}
     dom = max(ku, key=ku.get)
     if dom == "scan":
-        roof = {"bound": "mfma", "achieved": kernels["scan"]["tflops"], "peak": PEAK_TFLOPS["fp32"],
+        # its contraction runs on bf16 MFMAs (hi/lo operand parts): priced at the bf16 dense peak
+        roof = {"bound": "mfma", "achieved": kernels["scan"]["tflops"], "peak": PEAK_TFLOPS["bf16"],
                 "unit": "TFLOP/s"}
     elif dom == "output":
         roof = {"bound": "mfma", "achieved": kernels["output"]["tflops"], "peak": PEAK_TFLOPS["bf16"],
@@ -393,7 +463,7 @@ def main():
     if not args.no_decode:
         res["decode"] = bench_decode(I.WORKLOADS[4], args.decode_steps, args.warmup)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"] = cpu_baseline(wl, I.WORKLOADS[4])
     print(json.dumps(res), flush=True)
 
 
