@@ -146,6 +146,25 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
 
+/* lola_prefill_chunk for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results, with the workspace taken from a library-owned
+ * static device array of LOLA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which
+ * each GPU the library runs on holds from its first use until the process
+ * ends.  This call allocates and frees nothing (the first call on a device
+ * only looks up that device's copy of the array).
+ *   Errors: as lola_prefill_chunk, and LOLA_ERR_WORKSPACE if
+ *   lola_prefill_workspace_bytes(cfg, batch, n_tokens) exceeds
+ *   LOLA_NOALLOC_SCRATCH_BYTES (e.g. more than one 4096-token call of the
+ *   32/8-head, head_dim 128 layer at batch 1), LOLA_ERR_INVALID_ARG if
+ *   `stream` belongs to a device other than the current one.
+ *   Every call on one GPU shares the array: calls that overlap in time on one
+ *   GPU (other streams, other host threads) race and must be serialised by
+ *   the caller; calls in order on one stream are safe. */
+#define LOLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lola_status lola_prefill_chunk_noalloc(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens,
+                                       const void* q, const void* k, const void* v, void* out, void* stream);
+
 /* lola_prefill_chunk with a token count per sequence, for batches whose
  * sequences advance by different amounts in one call (prefill chunks of
  * several lengths, single decode tokens, idle sequences).  The method runs

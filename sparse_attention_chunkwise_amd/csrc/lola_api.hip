@@ -3,6 +3,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lola_decode.h"
 #include "lola_internal.h"
 #include "lola_misc.h"
@@ -13,7 +15,42 @@
 
 using namespace lola;
 
+// Workspace of lola_prefill_chunk_noalloc: one array per GPU, held from the first
+// use until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns for the current
+// device (kept in scratch_ptr) may be passed to kernels.  Every call on a GPU uses
+// the same array and leaves its contents behind; the kernels clear what must start
+// at zero (the prologue zeroes the split scan's exchange slots and counters).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's `scratch` (looked up once per device, with the
+// stream's device current).
+lola_status noalloc_scratch(hipStream_t stream, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LOLA_ERR_HIP;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return LOLA_ERR_HIP;
+        if (sdev != dev) return LOLA_ERR_INVALID_ARG;  // the stream must belong to the current device
+    }
+    if (dev < 0 || dev >= kMaxDevices) return LOLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LOLA_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return LOLA_OK;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -285,6 +322,21 @@ lola_status lola_prefill_chunk_timed(const lola_config* cfg, void* state, int32_
 {
     return prefill_impl(cfg, state, batch, n_tokens, nullptr, q, k, v, out, workspace, workspace_bytes, stream,
                         events);
+}
+
+lola_status lola_prefill_chunk_noalloc(const lola_config* cfg, void* state, int32_t batch, int32_t n_tokens,
+                                       const void* q, const void* k, const void* v, void* out, void* stream)
+{
+    Dims d;
+    lola_status st = make_dims(cfg, &d);
+    if (st != LOLA_OK) return st;
+    if ((st = check_batch(batch, d)) != LOLA_OK) return st;
+    if (n_tokens < 1) return LOLA_ERR_INVALID_ARG;
+    if (ws_layout(d, batch, n_tokens).total > kNoallocScratchBytes) return LOLA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != LOLA_OK) return st;
+    return prefill_impl(cfg, state, batch, n_tokens, nullptr, q, k, v, out, ws, kNoallocScratchBytes, stream,
+                        nullptr);
 }
 
 lola_status lola_prefill_ragged(const lola_config* cfg, void* state, int32_t batch, int32_t max_tokens,

@@ -22,8 +22,9 @@ _STATUS = {0: "LOLA_OK", -1: "LOLA_ERR_INVALID_ARG", -2: "LOLA_ERR_UNSUPPORTED",
 
 # Every symbol include/lola.h declares.
 EXPORTS = ("lola_state_bytes", "lola_prefill_workspace_bytes", "lola_init_state", "lola_prefill_chunk",
-           "lola_prefill_chunk_timed", "lola_prefill_ragged", "lola_decode_step", "lola_read_cache",
-           "lola_check_state", "lola_status_string")
+           "lola_prefill_chunk_timed", "lola_prefill_chunk_noalloc", "lola_prefill_ragged", "lola_decode_step",
+           "lola_read_cache", "lola_check_state", "lola_status_string")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LolaError(RuntimeError):
@@ -60,6 +61,8 @@ def lib():
         L.lola_prefill_chunk.restype = ctypes.c_int
         L.lola_prefill_chunk_timed.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.lola_prefill_chunk_timed.restype = ctypes.c_int
+        L.lola_prefill_chunk_noalloc.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp]
+        L.lola_prefill_chunk_noalloc.restype = ctypes.c_int
         L.lola_prefill_ragged.argtypes = [cp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lola_prefill_ragged.restype = ctypes.c_int
         L.lola_decode_step.argtypes = [cp, vp, i32, vp, vp, vp, vp, vp]
@@ -140,6 +143,16 @@ def prefill(layer, state, q, k, v, out=None, workspace=None):
     _check(lib().lola_prefill_chunk(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()), "lola_prefill_chunk")
+    return out
+
+
+def prefill_noalloc(layer, state, q, k, v, out=None):
+    """lola_prefill_chunk_noalloc: as prefill(), with the library's static device scratch."""
+    B, n = k.shape[0], k.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check(lib().lola_prefill_chunk_noalloc(ctypes.byref(config(layer)), _ptr(state), B, n, _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(out), _stream()), "lola_prefill_chunk_noalloc")
     return out
 
 
