@@ -9,7 +9,11 @@ Parity status of each oracle function (what pins it, see tests/):
              shift invariance) and a NumPy restatement.
   lo_sre  -- closed forms (zero for a state holding only that pair, mean-value
              state, scale invariance, empty state).
-  lo_run  -- reductions to causal softmax attention (w >= T) and to causal
+  lo_run  -- (policies other than the SRE: closed forms for the FIFO cache,
+             the attention-weight scorer with one query head and the
+             approximation-error scorer with a constant feature map, and an
+             independent NumPy replay of every policy)
+             reductions to causal softmax attention (w >= T) and to causal
              linear attention (w = 0, C = 0), chunk-size independence at
              C = 0, per-key-weight brute force, from-scratch recomputation of
              every interval's scores and ranking, conservation laws, a hand
@@ -42,7 +46,7 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("feat_half", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("cache_cap", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("scale", ctypes.c_double)]
+                ("chunk", ctypes.c_int32), ("policy", ctypes.c_int32), ("scale", ctypes.c_double)]
 
 
 class _Log(ctypes.Structure):
@@ -114,7 +118,7 @@ class Oracle:
         self.B = batch
         L = layer
         self._cfg = _Cfg(L.n_q_heads, L.n_kv_heads, L.head_dim, L.feat_half, L.window,
-                         L.cache_cap, L.chunk, float(L.softmax_scale))
+                         L.cache_cap, L.chunk, int(L.policy), float(L.softmax_scale))
         if _handle is None:
             W = _f64(W)
             assert W.shape == (L.n_kv_heads, L.feat_half, L.head_dim), W.shape
@@ -171,7 +175,7 @@ class Oracle:
         cm = None if chain_mask is None else np.ascontiguousarray(chain_mask, dtype=np.uint8)
         rm = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8)
         nt = nthreads or min(os.cpu_count() or 1, B * L.n_kv_heads, 16)
-        rc = self.lib.lo_run(self._h, n, _ptr(q) if want_out else None, _ptr(k), _ptr(v),
+        rc = self.lib.lo_run(self._h, n, _ptr(q), _ptr(k), _ptr(v),
                              _ptr(out), _ptr(forced), ctypes.byref(lg) if lg is not None else None,
                              _ptr(cm), _ptr(rm), nt)
         if rc == -2:

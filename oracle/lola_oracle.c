@@ -42,7 +42,8 @@
  * Readings where the pages are silent (order of read and management, pending
  * keys, empty state, tie order, window membership, combination weights,
  * softmax scale) follow the list in the design notes; each is marked
- * "reading:" where it is used below.
+ * "reading:" where it is used below.  The scoring and cache policies other
+ * than the SRE (lo_cfg.policy) are described at their enum.
  *
  * Everything is fp64, loops are plain, nothing is blocked or fused.
  */
@@ -55,8 +56,32 @@
 typedef struct {
     int32_t n_q_heads, n_kv_heads, head_dim, feat_half;
     int32_t window, cache_cap, chunk;
-    double scale; /* tau on q.k; 0 -> 1/sqrt(head_dim) (reading: no scale inside phi) */
+    int32_t policy; /* how candidates are scored, one of lo_policy */
+    double scale;   /* tau on q.k; 0 -> 1/sqrt(head_dim) (reading: no scale inside phi) */
 } lo_cfg;
+
+/* Scoring and cache policies.  The method scores every candidate by its SRE at
+ * every interval ("Inferentiestrategie", steps 1-2).  Step 2 also says the kept
+ * pairs live in a min-heap or a FIFO depending on the implementation, and the
+ * summary's contributions and ablations name two other scorers, the magnitude
+ * of the attention weights and the softmax approximation error, without
+ * formulas.  Readings implemented here (all keep the C highest scores, ties to
+ * the older position, exactly as the SRE policy):
+ *   LO_SRE        the method: SRE against the interval-start state, every
+ *                 candidate rescored at every interval.
+ *   LO_SRE_STALE  min-heap of stale scores: a pair is scored by SRE once, in
+ *                 the interval in which it leaves the window; a cached pair
+ *                 keeps that score and is never rescored.
+ *   LO_FIFO       first in, first out: the score is the position, so the C
+ *                 most recent candidates stay and the oldest are folded.
+ *   LO_ATTN       attention-weight magnitude: with q_h (h in the KV head's
+ *                 query heads) the last query of the interval, the score of u
+ *                 is sum_h softmax over the candidates of tau q_h.k_u.
+ *   LO_KERR       softmax approximation error: with p_hu that softmax weight
+ *                 and l_hu = phi(q_h).phi(k_u) / sum over the candidates of
+ *                 phi(q_h).phi(k) the weight linear attention gives the same
+ *                 candidate, the score is sum_h |p_hu - l_hu|. */
+enum { LO_SRE = 0, LO_SRE_STALE = 1, LO_FIFO = 2, LO_ATTN = 3, LO_KERR = 4 };
 
 /* Optional per-interval log, indexed [b][g][interval] (and a candidate or
  * cache slot index last).  Any pointer may be NULL. */
@@ -65,7 +90,7 @@ typedef struct {
     int32_t max_cand;      /* maxU: candidate slots per interval (>= C + L) */
     int32_t* n_cand;       /* [B][Hkv][NI]            |U| */
     int64_t* cand_pos;     /* [B][Hkv][NI][maxU]       candidate positions, cache first then leaving keys */
-    double* cand_sre;      /* [B][Hkv][NI][maxU]       their self-recall errors */
+    double* cand_sre;      /* [B][Hkv][NI][maxU]       their scores (self-recall errors for LO_SRE) */
     int64_t* own_kept;     /* [B][Hkv][NI][C]          the oracle's own kept set, by rank, -1 padded */
 } lo_log;
 
@@ -77,6 +102,7 @@ typedef struct {
     int cn;                  /* cache entries held (<= C), no order */
     int64_t* cpos;
     double *ck, *cv;         /* [C][D] */
+    double* cscore;          /* [C] the score each cached pair was kept with */
     int64_t n_folded;
 } lo_chain;
 
@@ -158,13 +184,14 @@ static void chain_alloc(lo_chain* c, const lo_cfg* cfg)
     c->cpos = (int64_t*)calloc((size_t)(C > 0 ? C : 1), sizeof(int64_t));
     c->ck = (double*)calloc((size_t)(C > 0 ? C : 1) * D, sizeof(double));
     c->cv = (double*)calloc((size_t)(C > 0 ? C : 1) * D, sizeof(double));
+    c->cscore = (double*)calloc((size_t)(C > 0 ? C : 1), sizeof(double));
     c->n_folded = 0;
 }
 
 static void chain_free(lo_chain* c)
 {
     free(c->H); free(c->s); free(c->wpos); free(c->wk); free(c->wv);
-    free(c->cpos); free(c->ck); free(c->cv);
+    free(c->cpos); free(c->ck); free(c->cv); free(c->cscore);
 }
 
 static void chain_copy(lo_chain* dst, const lo_chain* src, const lo_cfg* cfg)
@@ -181,6 +208,7 @@ static void chain_copy(lo_chain* dst, const lo_chain* src, const lo_cfg* cfg)
     memcpy(dst->cpos, src->cpos, sizeof(int64_t) * (size_t)C);
     memcpy(dst->ck, src->ck, sizeof(double) * (size_t)C * D);
     memcpy(dst->cv, src->cv, sizeof(double) * (size_t)C * D);
+    memcpy(dst->cscore, src->cscore, sizeof(double) * (size_t)C);
     dst->n_folded = src->n_folded;
 }
 
@@ -188,7 +216,7 @@ lo_state* lo_create(const lo_cfg* cfg, int B, const double* W)
 {
     if (!cfg || B <= 0 || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads != 0 ||
         cfg->head_dim <= 0 || cfg->feat_half <= 0 || cfg->window < 0 || cfg->cache_cap < 0 ||
-        cfg->chunk < 1)
+        cfg->chunk < 1 || cfg->policy < LO_SRE || cfg->policy > LO_KERR)
         return NULL;
     lo_state* st = (lo_state*)calloc(1, sizeof(lo_state));
     st->cfg = *cfg;
@@ -426,11 +454,49 @@ static int run_interval(run_job* jb, int b, int g, int ci, int64_t t0c, int64_t 
         Upos[c->cn + i] = Rpos[i];
         memcpy(Uphi + (size_t)(c->cn + i) * F, Rphi + (size_t)i * F, sizeof(double) * F);
     }
-    /* score every candidate against the interval-start state (reading) */
+    /* score every candidate (reading: SRE against the interval-start state) */
     for (int u = 0; u < nU; ++u) {
         cand[u].idx = u;
         cand[u].pos = Upos[u];
         cand[u].e = lo_sre(F, D, c->H, c->s, Uphi + (size_t)u * F, Uv[u]);
+    }
+    if (cfg->policy == LO_SRE_STALE) {
+        /* a cached pair keeps the score it was kept with */
+        for (int u = 0; u < c->cn; ++u) cand[u].e = c->cscore[u];
+    } else if (cfg->policy == LO_FIFO) {
+        for (int u = 0; u < nU; ++u) cand[u].e = (double)Upos[u];
+    } else if ((cfg->policy == LO_ATTN || cfg->policy == LO_KERR) && nU > 0) {
+        /* the interval's last query, every query head of this KV head */
+        const int64_t tl = e - 1;
+        double* lgt = (double*)malloc(sizeof(double) * (size_t)nU);
+        double* kap = (double*)malloc(sizeof(double) * (size_t)nU);
+        double* phq = (double*)malloc(sizeof(double) * F);
+        for (int u = 0; u < nU; ++u) cand[u].e = 0.0;
+        for (int h = g * G; h < (g + 1) * G; ++h) {
+            const double* qv = jb->q + (((size_t)b * n + (size_t)(tl - t0c)) * Hq + h) * D;
+            double mx = -INFINITY, zs = 0.0, ks = 0.0;
+            for (int u = 0; u < nU; ++u) {
+                double dot = 0.0;
+                for (int j = 0; j < D; ++j) dot += qv[j] * Uk[u][j];
+                lgt[u] = tau * dot;
+                if (lgt[u] > mx) mx = lgt[u];
+            }
+            for (int u = 0; u < nU; ++u) zs += exp(lgt[u] - mx);
+            if (cfg->policy == LO_KERR) {
+                lo_phi(Wg, Fh, D, qv, phq);
+                for (int u = 0; u < nU; ++u) {
+                    double kk = 0.0;
+                    for (int f = 0; f < F; ++f) kk += phq[f] * Uphi[(size_t)u * F + f];
+                    kap[u] = kk;
+                    ks += kk;
+                }
+            }
+            for (int u = 0; u < nU; ++u) {
+                const double p = exp(lgt[u] - mx) / zs;
+                cand[u].e += cfg->policy == LO_ATTN ? p : fabs(p - kap[u] / ks);
+            }
+        }
+        free(lgt); free(kap); free(phq);
     }
     const lo_log* lg = jb->log;
     size_t li = ((size_t)b * Hkv + g) * (size_t)(lg ? lg->max_intervals : 0) + (size_t)ci;
@@ -490,9 +556,11 @@ static int run_interval(run_job* jb, int b, int g, int ci, int64_t t0c, int64_t 
     int64_t* npos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(C > 0 ? C : 1));
     double* nk = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1) * D);
     double* nv = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1) * D);
+    double* nsc = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
     int cn = 0;
     for (int u = 0; u < nU; ++u) {
         if (!keep[u]) continue;
+        nsc[cn] = cand[u].e;
         npos[cn] = Upos[u];
         memcpy(nk + (size_t)cn * D, Uk[u], sizeof(double) * D);
         memcpy(nv + (size_t)cn * D, Uv[u], sizeof(double) * D);
@@ -513,12 +581,13 @@ static int run_interval(run_job* jb, int b, int g, int ci, int64_t t0c, int64_t 
     memcpy(c->cpos, npos, sizeof(int64_t) * (size_t)cn);
     memcpy(c->ck, nk, sizeof(double) * (size_t)cn * D);
     memcpy(c->cv, nv, sizeof(double) * (size_t)cn * D);
+    memcpy(c->cscore, nsc, sizeof(double) * (size_t)cn);
     c->wn = wn;
     memcpy(c->wpos, wpos2, sizeof(int64_t) * (size_t)wn);
     memcpy(c->wk, wk2, sizeof(double) * (size_t)wn * D);
     memcpy(c->wv, wv2, sizeof(double) * (size_t)wn * D);
 
-    free(npos); free(nk); free(nv); free(wpos2); free(wk2); free(wv2);
+    free(npos); free(nk); free(nv); free(nsc); free(wpos2); free(wk2); free(wv2);
     free(keep); free(cand); free(Upos); free(Uv); free(Uk); free(Uphi);
     free(Rpos); free(Rk); free(Rv); free(Rphi);
     return 0;
@@ -567,6 +636,7 @@ int lo_run(lo_state* st, int n, const double* q, const double* k, const double* 
            const uint8_t* row_mask, int nthreads)
 {
     if (!st || n <= 0 || !k || !v || (out && !q)) return -1;
+    if ((st->cfg.policy == LO_ATTN || st->cfg.policy == LO_KERR) && !q) return -1; /* they score with q */
     int NI = (n + st->cfg.chunk - 1) / st->cfg.chunk;
     if (log && (log->max_intervals < NI || log->max_cand < st->cfg.cache_cap + st->cfg.chunk)) return -1;
     if (nthreads < 1) nthreads = 1;

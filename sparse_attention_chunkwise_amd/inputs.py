@@ -44,6 +44,7 @@ class LayerConfig:
     chunk: int
     io_dtype: str  # "f32" or "bf16"
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(head_dim)
+    policy: int = 0  # scoring / cache policy: 0 SRE, 1 stale SRE (min-heap), 2 FIFO, 3 attention weight, 4 softmax error
 
     @property
     def feat_dim(self) -> int:

@@ -70,7 +70,7 @@ def brute_outputs(layer, W, Q, K, V, cache_sets, t_start=0):
     return out
 
 
-def replay_selection(layer, W, K, V, T, choose=None):
+def replay_selection(layer, W, K, V, T, choose=None, Q=None):
     """Recompute every interval's candidates, scores and kept set from scratch.
 
     Candidates at interval [a, e): the cache plus positions max(0,a-w)..e-1-w.
@@ -81,6 +81,12 @@ def replay_selection(layer, W, K, V, T, choose=None):
     choose(b, g, c, U, scores, own) may replace the kept set `own` (the first
     min(C, |U|) by score descending, position ascending) by another list of
     positions; the rest of the candidates are folded.
+    layer.policy other than 0 replaces the SRE as the score (Q gives the
+    queries of the query-based scorers): 1 a cached pair keeps the score it
+    had when it left the window, 2 the position, 3 the sum over the KV head's
+    query heads of the softmax weight the interval's last query gives the
+    candidate among all candidates, 4 the sum of |softmax weight - linear
+    weight| with linear weight phi(q).phi(k) normalised over the candidates.
     Returns per chain a list of dicts (cand positions, scores, own and kept
     sets) and, per chain, the folded positions in fold order.
     """
@@ -93,6 +99,7 @@ def replay_selection(layer, W, K, V, T, choose=None):
             phK = phi_rows(W[g], K[b, :, g])
             Vg = V[b, :, g].astype(np.float64)
             folded, S, steps = [], [], []
+            kept_score = {}
             for a in range(0, T, L):
                 e = min(a + L, T)
                 E = list(range(max(0, a - w), e - w))
@@ -103,10 +110,26 @@ def replay_selection(layer, W, K, V, T, choose=None):
                 else:
                     r = np.zeros((len(U), Vg.shape[1]))
                 sc = ((r - Vg[U]) ** 2).sum(axis=1) if U else np.zeros(0)
+                if layer.policy == 1:
+                    sc = np.array([kept_score[u] if u in kept_score else x for u, x in zip(U, sc)])
+                elif layer.policy == 2:
+                    sc = np.array(U, np.float64)
+                elif layer.policy in (3, 4) and U:
+                    G = layer.group
+                    sc = np.zeros(len(U))
+                    for h in range(g * G, (g + 1) * G):
+                        q = Q[b, e - 1, h].astype(np.float64)
+                        p = scipy.special.softmax(layer.scale * (K[b, U, g].astype(np.float64) @ q))
+                        if layer.policy == 3:
+                            sc += p
+                        else:
+                            lin = phK[U] @ phi_rows(W[g], q[None])[0]
+                            sc += np.abs(p - lin / lin.sum())
                 order = sorted(range(len(U)), key=lambda i: (-sc[i], U[i]))
                 own = [U[i] for i in order[: min(C, len(U))]]
                 keep = own if choose is None else list(choose(b, g, len(steps), U, sc, own))
                 gone = [u for u in U if u not in set(keep)]
+                kept_score = {u: x for u, x in zip(U, sc) if u in set(keep)}
                 steps.append({"U": U, "sre": sc, "keep": set(keep), "own": set(own), "order": order,
                               "folded": list(folded)})
                 folded.extend(gone)
@@ -379,6 +402,131 @@ def check_forced_selection(lib):
         raise AssertionError(f"forced set with a {bad} entry accepted")
 
 
+POLICY_LAYERS = [
+    # (layer without the policy, T): several query heads per KV head, L = 1, L > w
+    (LayerConfig(4, 2, 8, 3, 3, 3, 4, "f32"), 37),
+    (LayerConfig(2, 1, 8, 4, 2, 2, 1, "f32"), 21),
+    (LayerConfig(3, 1, 16, 4, 2, 4, 6, "f32"), 44),
+]
+
+
+def _with_policy(layer, policy):
+    return LayerConfig(layer.n_q_heads, layer.n_kv_heads, layer.head_dim, layer.feat_half, layer.window,
+                       layer.cache_cap, layer.chunk, layer.io_dtype, layer.softmax_scale, policy)
+
+
+def check_policy_replay(lib):
+    """Every scoring / cache policy: candidates, logged scores and kept sets equal an
+    independent NumPy replay of the policy, and the outputs equal the per-key-weight
+    brute force under the oracle's own cache sets."""
+    for policy in (1, 2, 3, 4):
+        for base, T in POLICY_LAYERS:
+            lay = _with_policy(base, policy)
+            B = 2
+            W, Q, K, V = _case(lay, T, B=B, seed=20 + policy)
+            o, log = oracle.Oracle(lay, B, W, lib).run(Q, K, V, log=True)
+            rep = replay_selection(lay, W, K, V, T, Q=Q)
+            for b in range(B):
+                for g in range(lay.n_kv_heads):
+                    for c, st in enumerate(rep[b][g][:-1]):
+                        nU = int(log["n_cand"][b, g, c])
+                        pos = [int(p) for p in log["cand_pos"][b, g, c, :nU]]
+                        assert sorted(pos) == sorted(st["U"]), (policy, b, g, c)
+                        got = dict(zip(pos, log["cand_sre"][b, g, c, :nU]))
+                        for u, x in zip(st["U"], st["sre"]):
+                            assert abs(got[u] - x) <= 1e-9 * max(1.0, abs(x)), (policy, b, g, c, u, got[u], x)
+                        kept = set(int(p) for p in log["own_kept"][b, g, c] if p >= 0)
+                        assert kept == st["keep"], (policy, b, g, c, kept, st["keep"])
+            ref = brute_outputs(lay, W, Q, K, V, cache_sets_from_log(log, B, lay.n_kv_heads))
+            np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+
+
+def check_fifo_closed_form(lib):
+    """FIFO: after the interval [a, e) the cache holds exactly the C most recent
+    positions that have left the window, [max(0, e-w-C), e-w), and the state holds
+    every older pair."""
+    lay = _with_policy(LayerConfig(2, 2, 8, 3, 3, 4, 5, "f32"), 2)
+    T = 41
+    W, Q, K, V = _case(lay, T, seed=31)
+    orc = oracle.Oracle(lay, 1, W, lib)
+    for a in range(0, T, lay.chunk):
+        e = min(a + lay.chunk, T)
+        orc.run(Q[:, a:e], K[:, a:e], V[:, a:e])
+        hi = e - lay.window
+        want = list(range(max(0, hi - lay.cache_cap), max(0, hi)))
+        for g in range(2):
+            ch = orc.chain(0, g)
+            assert ch["cache_pos"].tolist() == want, (a, g, ch["cache_pos"].tolist(), want)
+            old = list(range(0, max(0, hi - lay.cache_cap)))
+            pk = phi_rows(W[g], K[0, old, g]) if old else np.zeros((0, 6))
+            np.testing.assert_allclose(ch["H"], pk.T @ V[0, old, g] if old else 0 * ch["H"], atol=1e-12)
+
+
+def check_attn_one_head_is_top_dot(lib):
+    """Attention-weight scorer with one query head per KV head: softmax is monotone, so
+    the kept set is the C candidates with the largest q.k for the interval's last query
+    (older position first on a tie)."""
+    lay = _with_policy(LayerConfig(2, 2, 8, 3, 3, 3, 4, "f32"), 3)
+    T = 33
+    W, Q, K, V = _case(lay, T, seed=32)
+    _, log = oracle.Oracle(lay, 1, W, lib).run(Q, K, V, log=True)
+    for g in range(2):
+        for c in range(log["n_cand"].shape[2]):
+            nU = int(log["n_cand"][0, g, c])
+            if nU <= lay.cache_cap:
+                continue
+            pos = [int(p) for p in log["cand_pos"][0, g, c, :nU]]
+            e = min((c + 1) * lay.chunk, T)
+            dots = K[0, pos, g] @ Q[0, e - 1, g]
+            order = sorted(range(nU), key=lambda i: (-dots[i], pos[i]))
+            want = set(pos[i] for i in order[: lay.cache_cap])
+            kept = set(int(p) for p in log["own_kept"][0, g, c] if p >= 0)
+            assert kept == want, (g, c)
+
+
+def check_kerr_constant_features(lib):
+    """Softmax-approximation-error scorer with W = 0: every feature vector is the same,
+    so the linear weight of each candidate is 1/|U| and the score is
+    sum_h |softmax weight - 1/|U||."""
+    lay = _with_policy(LayerConfig(4, 2, 8, 3, 3, 3, 4, "f32"), 4)
+    T = 30
+    _, Q, K, V = _case(lay, T, seed=33)
+    W = np.zeros((2, 3, 8))
+    _, log = oracle.Oracle(lay, 1, W, lib).run(Q, K, V, log=True)
+    G = lay.group
+    for g in range(2):
+        for c in range(log["n_cand"].shape[2]):
+            nU = int(log["n_cand"][0, g, c])
+            if nU == 0:
+                continue
+            pos = [int(p) for p in log["cand_pos"][0, g, c, :nU]]
+            e = min((c + 1) * lay.chunk, T)
+            want = np.zeros(nU)
+            for h in range(g * G, (g + 1) * G):
+                p = scipy.special.softmax(lay.scale * (K[0, pos, g] @ Q[0, e - 1, h]))
+                want += np.abs(p - 1.0 / nU)
+            np.testing.assert_allclose(log["cand_sre"][0, g, c, :nU], want, rtol=1e-12, atol=1e-15)
+
+
+def check_stale_scores_never_change(lib):
+    """Stale-score min-heap: the score logged for a cached pair in every later interval
+    is the SRE it had in the interval in which it left the window."""
+    lay = _with_policy(LayerConfig(2, 1, 8, 3, 2, 3, 3, "f32"), 1)
+    T = 45
+    W, Q, K, V = _case(lay, T, seed=34)
+    _, log = oracle.Oracle(lay, 1, W, lib).run(Q, K, V, log=True)
+    first = {}
+    for c in range(log["n_cand"].shape[2]):
+        nU = int(log["n_cand"][0, 0, c])
+        for p, x in zip(log["cand_pos"][0, 0, c, :nU], log["cand_sre"][0, 0, c, :nU]):
+            p = int(p)
+            if p in first:
+                assert x == first[p], (c, p)
+            else:
+                first[p] = x
+    assert len(first) > lay.cache_cap + 5
+
+
 def check_conservation(lib):
     """1^T s = 2 * folded count, column sums of H = 2 * sum of folded values,
     and window + cache + folded counts add up to the tokens seen."""
@@ -506,6 +654,11 @@ ALL_CHECKS = [
     check_per_key_weights,
     check_selection_replay,
     check_forced_selection,
+    check_policy_replay,
+    check_fifo_closed_form,
+    check_attn_one_head_is_top_dot,
+    check_kerr_constant_features,
+    check_stale_scores_never_change,
     check_conservation,
     check_kept_outrank_folded,
     check_tie_order,

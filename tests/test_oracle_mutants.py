@@ -36,6 +36,15 @@ MUTANTS = {
                                   "jb->forced + (((size_t)b * Hkv + 0) * jb->NI + ci)")],
     "forced_set_of_first_interval": [("jb->forced + (((size_t)b * Hkv + g) * jb->NI + ci)",
                                       "jb->forced + (((size_t)b * Hkv + g) * jb->NI + 0)")],
+    # scoring and cache policies other than the SRE
+    "stale_scores_refreshed": [("for (int u = 0; u < c->cn; ++u) cand[u].e = c->cscore[u];",
+                                "for (int u = 0; u < c->cn; ++u) cand[u].e += 0.0 * c->cscore[u];")],
+    "fifo_keeps_oldest": [("for (int u = 0; u < nU; ++u) cand[u].e = (double)Upos[u];",
+                           "for (int u = 0; u < nU; ++u) cand[u].e = -(double)Upos[u];")],
+    "attn_weights_not_normalised": [("const double p = exp(lgt[u] - mx) / zs;",
+                                     "const double p = exp(lgt[u] - mx) / (zs > 0.0 ? 1.0 : zs);")],
+    "scorers_use_first_query": [("const int64_t tl = e - 1;", "const int64_t tl = a;")],
+    "kerr_signed_difference": [("fabs(p - kap[u] / ks)", "(p - kap[u] / ks)")],
     "forced_kept_pair_also_folded": [("        if (keep[u]) continue;\n        const double* ph = Uphi",
                                       "        if (keep[u] && !(jb->forced && u == 0)) continue;\n"
                                       "        const double* ph = Uphi")],
