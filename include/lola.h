@@ -78,6 +78,36 @@ typedef enum {
 
 typedef enum { LOLA_F32 = 0, LOLA_BF16 = 1 } lola_dtype;
 
+/* How the candidates of an interval (the cached pairs and the pairs leaving the
+ * window) are scored; every policy keeps the C highest scores, the older
+ * position first on a tie, and folds the rest.  The method is LOLA_POLICY_SRE
+ * (summary, "Inferentiestrategie", steps 1-2).  The others are the summary's
+ * alternatives -- step 2's min-heap or FIFO cache structure, and the scorers its
+ * contributions and ablations compare against the SRE (attention-weight
+ * magnitude, softmax approximation error) -- which it names without formulas;
+ * this library reads them as:
+ *   LOLA_POLICY_SRE_STALE   a pair is scored by its SRE once, in the interval in
+ *                           which it leaves the window; a cached pair keeps that
+ *                           score (a min-heap of stale scores)
+ *   LOLA_POLICY_FIFO        the score is the position: the C most recent stay
+ *   LOLA_POLICY_ATTN        sum over the KV head's query heads of the softmax
+ *                           weight that the interval's last query gives the
+ *                           candidate among all candidates (scale softmax_scale)
+ *   LOLA_POLICY_SOFTMAX_ERR sum over those heads of |that softmax weight - the
+ *                           candidate's linear-attention weight
+ *                           phi(q).phi(k) / sum over the candidates|
+ * The policies other than LOLA_POLICY_SRE run in lola_prefill_chunk and
+ * lola_prefill_ragged (any token count, so n_tokens = 1 gives the token-by-
+ * token mode); lola_decode_step's fused kernel implements LOLA_POLICY_SRE only
+ * and returns LOLA_ERR_UNSUPPORTED for the others. */
+typedef enum {
+    LOLA_POLICY_SRE = 0,
+    LOLA_POLICY_SRE_STALE = 1,
+    LOLA_POLICY_FIFO = 2,
+    LOLA_POLICY_ATTN = 3,
+    LOLA_POLICY_SOFTMAX_ERR = 4
+} lola_policy;
+
 typedef struct {
     int32_t n_q_heads;     /* Hq; a multiple of n_kv_heads (query head h reads KV head h / (Hq/Hkv)) */
     int32_t n_kv_heads;    /* Hkv */
@@ -88,6 +118,7 @@ typedef struct {
     int32_t chunk;         /* L >= 1: update interval length of lola_prefill_chunk */
     int32_t io_dtype;      /* lola_dtype */
     float softmax_scale;   /* tau on q.k; <= 0 selects 1/sqrt(head_dim) */
+    int32_t policy;        /* one of lola_policy; 0 = the SRE of the method */
 } lola_config;
 
 /* Bytes of the state buffer for `batch` sequences: a header, W, and per

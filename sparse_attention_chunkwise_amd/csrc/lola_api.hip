@@ -67,6 +67,7 @@ lola_status make_dims(const lola_config* cfg, Dims* d)
     if (cfg->window > kMaxWindow || cfg->cache_cap > kMaxCache || cfg->chunk > kMaxChunk) return LOLA_ERR_UNSUPPORTED;
     if (cfg->io_dtype != LOLA_F32 && cfg->io_dtype != LOLA_BF16) return LOLA_ERR_UNSUPPORTED;
     if (!(cfg->softmax_scale == cfg->softmax_scale)) return LOLA_ERR_INVALID_ARG;  // NaN
+    if (cfg->policy < LOLA_POLICY_SRE || cfg->policy > LOLA_POLICY_SOFTMAX_ERR) return LOLA_ERR_UNSUPPORTED;
     d->Hq = cfg->n_q_heads;
     d->Hkv = cfg->n_kv_heads;
     d->D = cfg->head_dim;
@@ -79,6 +80,7 @@ lola_status make_dims(const lola_config* cfg, Dims* d)
     d->io = cfg->io_dtype;
     d->esize = cfg->io_dtype == LOLA_BF16 ? 2 : 4;
     d->tau = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
+    d->policy = cfg->policy;
     return LOLA_OK;
 }
 
@@ -96,6 +98,7 @@ uint64_t cfg_hash(const lola_config* c, int batch)
     mix((uint32_t)c->n_q_heads); mix((uint32_t)c->n_kv_heads); mix((uint32_t)c->head_dim);
     mix((uint32_t)c->feat_half); mix((uint32_t)c->window); mix((uint32_t)c->cache_cap);
     mix((uint32_t)c->chunk); mix((uint32_t)c->io_dtype); mix(sc); mix((uint32_t)batch);
+    if (c->policy != 0) mix(0x9e3779b9u ^ (uint32_t)c->policy);
     return h;
 }
 
@@ -157,8 +160,9 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     size_t split_lds = 0;
     if constexpr (sizeof(T) == 2) {
         split_lds = split_smem<F>().total;
-        // as many candidate groups per column slice (4, 2, then 1) as the device holds at once
-        if (split_allowed())
+        // as many candidate groups per column slice (4, 2, then 1) as the device holds at
+        // once; the scoring policies other than the SRE run in the one-workgroup scan
+        if (split_allowed() && d.policy == LOLA_POLICY_SRE)
             for (int g : {4, 2, 1})
                 if (split_fits(scan_split_kernel<D, F>, split_blocks(D, chains, g), split_lds)) {
                     pu = g;
@@ -359,6 +363,7 @@ lola_status lola_decode_step(const lola_config* cfg, void* state, int32_t batch,
     if (!state || !q || !k || !v || !out) return LOLA_ERR_INVALID_ARG;
     if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LOLA_ERR_INVALID_ARG;
+    if (d.policy != LOLA_POLICY_SRE) return LOLA_ERR_UNSUPPORTED;  // lola_prefill_chunk(n_tokens = 1) runs it
     Args a = base_args(cfg, d, batch, state);
     a.n = 1;
     a.NI = 1;

@@ -19,7 +19,7 @@ constexpr int kMaxCache = 1024;
 constexpr int kMaxChunk = 256;
 constexpr int kMaxCand = kMaxCache + kMaxChunk;  // |cache| + |leaving keys| per interval
 constexpr uint32_t kMagic = 0x414c4f4cu;         // "LOLA"
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 
 constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -59,6 +59,7 @@ struct Dims {
     int io;       // 0 = f32, 1 = bf16
     int esize;    // bytes per io element
     float tau;    // softmax scale on q.k
+    int policy;   // lola_policy
 };
 
 struct StateHeader {
@@ -76,13 +77,14 @@ static_assert(sizeof(StateHeader) == 32, "kernels test the first 32 bytes of a s
 //        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io |
 //        cache_phi [C][2F] bf16 (bf16 io only: phi of each cached key as hi and lo parts,
 //        each in MFMA operand order, so that a decode step scores the cache without
-//        recomputing the feature map)
+//        recomputing the feature map) | cache_score [C] f32 (the score each cached
+//        pair was kept with; the stale-score policy reads it back)
 // Every chain keeps its own token count so that concurrent chains of one
 // sequence never race on a shared counter.  The window ring slot of
 // position p is p % w.
 struct StateLayout {
     size_t W, Wb, chains, chain_bytes;
-    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi;
+    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi, oscore;
     size_t total;
 };
 
@@ -106,6 +108,7 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     s.ocache_k = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
     s.ocache_v = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
     s.ocphi = c;     c = align_up(c + (d.io == 1 ? sizeof(uint16_t) * 2 * (size_t)d.F * d.C : 0), 256);
+    s.oscore = c;    c = align_up(c + sizeof(float) * (size_t)(d.C > 0 ? d.C : 1), 256);
     s.chain_bytes = c;
     s.total = s.chains + c * (size_t)B * d.Hkv;
     return s;

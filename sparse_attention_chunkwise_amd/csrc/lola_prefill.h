@@ -42,6 +42,7 @@ struct Chain {
     template <typename T> __device__ T* cache_k() const { return (T*)(base + sl->ocache_k); }
     template <typename T> __device__ T* cache_v() const { return (T*)(base + sl->ocache_v); }
     __device__ uint16_t* cphi() const { return (uint16_t*)(base + sl->ocphi); }  // bf16 io
+    __device__ float* cscore() const { return (float*)(base + sl->oscore); }
 };
 
 __device__ __forceinline__ Chain chain_of(const Args& a, int chain)
@@ -385,7 +386,8 @@ constexpr int kFoldChunk = 64;  // folded pairs staged per fold chunk
 __host__ __device__ constexpr int scan_threads(int D) { return 4 * D; }  // D/16 waves
 
 struct ScanSmem {
-    size_t stage, part, ebits, keep, fold, memb, freed, keptE, cref, cpos, hist, s, dS, ucode, bcnt, misc, total;
+    size_t stage, part, ebits, keep, fold, memb, freed, keptE, cref, cpos, hist, s, dS, ucode, bcnt, cscore, qx, red,
+        misc, total;
     int sphi_stride, sv_stride;  // elements per staged phi row (bf16) / value row
 };
 
@@ -414,6 +416,9 @@ __host__ __device__ inline ScanSmem scan_smem(int D, int F, int C, int L, int es
     m.dS = off;    off += sizeof(float) * kBatch;
     m.ucode = off; off += sizeof(int) * U;
     m.bcnt = off;  off += sizeof(int) * 4 * ((U + 63) / 64);
+    m.cscore = off; off += sizeof(float) * Cp;         // score each cached pair was kept with
+    m.qx = off;    off += sizeof(float) * ((size_t)D + F);  // a query row and its features (query-based scorers)
+    m.red = off;   off += sizeof(float) * 2 * 16;       // per-wave partials of block reductions
     m.misc = off;  off += sizeof(int) * 16;
     m.total = align_up(off, 16);
     return m;
@@ -482,6 +487,9 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     float* dS = (float*)(smem + sm.dS);
     int* ucode = (int*)(smem + sm.ucode);  // candidate source: X row (>= 0) or call-start cache slot -code-1
     int* bcnt = (int*)(smem + sm.bcnt);
+    float* cscoreL = (float*)(smem + sm.cscore);
+    float* qxL = (float*)(smem + sm.qx);
+    float* red = (float*)(smem + sm.red);
     int* misc = (int*)(smem + sm.misc);
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
@@ -523,6 +531,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     for (int i = tid; i < cnt; i += NT) {
         cpos[i] = ch.cpos()[i];
         cref[i] = -(i + 1);
+        cscoreL[i] = ch.cscore()[i];
     }
     __syncthreads();
 
@@ -583,6 +592,94 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         auto cand_phi = [&](int u) -> const float* { return code_phi(ucode[u]); };
         auto cand_v = [&](int u) -> const T* { return code_v(ucode[u]); };
         auto cand_pos = [&](int u) -> int { return u < cnt ? cpos[u] : (int)(eS + (u - cnt)); };
+        // Block-wide max or sum of one value per thread (every thread gets the result).
+        auto block_op = [&](float x, bool is_max) -> float {
+            x = is_max ? wave_max(x) : wave_sum(x);
+            __syncthreads();  // the previous result has been read
+            if (lane == 0) red[wave] = x;
+            __syncthreads();
+            float r = red[0];
+            for (int ww = 1; ww < NW; ++ww) r = is_max ? fmaxf(r, red[ww]) : r + red[ww];
+            return r;
+        };
+        // Scores of the policies other than the SRE (lola_policy in lola.h): the stored
+        // score of each cached pair; or, head by head, the interval's last query against
+        // every candidate: its softmax weight among the candidates (fp32 logits, expf)
+        // and, for the approximation error, the candidate's normalised feature weight.
+        float* score = part;  // candidate u's score, once the SRE partials are summed
+        auto policy_scores = [&](int nUq, int64_t epq) {
+            const int pol = d.policy;
+            if (pol == LOLA_POLICY_SRE_STALE) {
+                for (int u = tid; u < cnt; u += NT) score[u] = cscoreL[u];
+                return;
+            }
+            if (pol != LOLA_POLICY_ATTN && pol != LOLA_POLICY_SOFTMAX_ERR) return;
+            float* lgt = part + U;      // (the partial-SRE rows of waves 1 and 2 are free now)
+            float* kap = part + 2 * U;
+            float* qv = qxL;
+            float* phq = qxL + D;
+            const int G = d.G;
+            const size_t trow = (size_t)(epq - 1 - t0);  // row of the interval's last query in this call
+            for (int u = tid; u < nUq; u += NT) score[u] = 0.f;
+            for (int h = 0; h < G; ++h) {
+                __syncthreads();  // the previous head's rows are consumed
+                const T* qp = (const T*)a.q + (((size_t)b * n + trow) * d.Hq + (size_t)g * G + h) * D;
+                for (int i = tid; i < D; i += NT) qv[i] = to_f32(qp[i]);
+                __syncthreads();
+                if (pol == LOLA_POLICY_SOFTMAX_ERR) {
+                    if (wave == 0) {  // phi(q) = [softmax(W q); softmax(-W q)], lane i < F/2 holds (W q)_i
+                        const float* Wg = (const float*)(a.state + a.sl.W) + (size_t)g * (F / 2) * D;
+                        float z = 0.f;
+                        if (lane < F / 2)
+                            for (int j = 0; j < D; ++j) z += Wg[(size_t)lane * D + j] * qv[j];
+                        const float zmax = wave_max(lane < F / 2 ? z : -INFINITY);
+                        const float zmin = -wave_max(lane < F / 2 ? -z : -INFINITY);
+                        const float e1 = lane < F / 2 ? expf(z - zmax) : 0.f;
+                        const float e2 = lane < F / 2 ? expf(zmin - z) : 0.f;
+                        const float s1 = wave_sum(e1), s2 = wave_sum(e2);
+                        if (lane < F / 2) {
+                            phq[lane] = e1 / s1;
+                            phq[F / 2 + lane] = e2 / s2;
+                        }
+                    }
+                    __syncthreads();
+                }
+                float mx = -INFINITY, ks = 0.f;
+                for (int u = tid; u < nUq; u += NT) {
+                    const int code = ucode[u];
+                    const T* kr = ref_k<T>(a, chain, b, g, code);
+                    float dot = 0.f;
+                    for (int j = 0; j < D; j += 4) {
+                        float x[4];
+                        load4(kr + j, x);
+                        dot += qv[j] * x[0] + qv[j + 1] * x[1] + qv[j + 2] * x[2] + qv[j + 3] * x[3];
+                    }
+                    const float l = d.tau * dot;
+                    lgt[u] = l;
+                    mx = fmaxf(mx, l);
+                    if (pol == LOLA_POLICY_SOFTMAX_ERR) {
+                        const float* pr = code_phi(code);
+                        float kk = 0.f;
+                        for (int f = 0; f < F; f += 4) {
+                            float x[4];
+                            load4(pr + f, x);
+                            kk += phq[f] * x[0] + phq[f + 1] * x[1] + phq[f + 2] * x[2] + phq[f + 3] * x[3];
+                        }
+                        kap[u] = kk;
+                        ks += kk;
+                    }
+                }
+                mx = block_op(mx, true);
+                if (pol == LOLA_POLICY_SOFTMAX_ERR) ks = block_op(ks, false);
+                float zs = 0.f;
+                for (int u = tid; u < nUq; u += NT) zs += expf(lgt[u] - mx);
+                zs = block_op(zs, false);
+                for (int u = tid; u < nUq; u += NT) {
+                    const float p = expf(lgt[u] - mx) / zs;
+                    score[u] += pol == LOLA_POLICY_ATTN ? p : fabsf(p - kap[u] / ks);
+                }
+            }
+        };
         __syncthreads();  // codes ready
 
         // ---- SRE in batches of 64 candidates ----
@@ -691,14 +788,23 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         }
         __syncthreads();  // per-wave partial errors complete
 
-        // ---- SRE totals and exact top-C on (SRE desc, position asc), all waves ----
+        // ---- scores: the SRE totals (part[u] once summed), or the policy's score ----
+        for (int u = tid; u < nU; u += NT) {
+            float e = part[u];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) e += part[ww * U + u];
+            score[u] = e;
+        }
+        if (d.policy != LOLA_POLICY_SRE && nU > 0) {  // block-uniform
+            __syncthreads();
+            policy_scores(nU, ep);
+        }
+        // ---- exact top-C on (score desc, position asc), all waves ----
         {
             uint32_t lo = 0xffffffffu, hi = 0u;
             for (int u = tid; u < nU; u += NT) {
-                float e = part[u];
-#pragma unroll
-                for (int ww = 1; ww < NW; ++ww) e += part[ww * U + u];
-                const uint32_t eb = __float_as_uint(e);
+                // scores are >= 0, so their bit patterns order like them; FIFO orders by position
+                const uint32_t eb = d.policy == LOLA_POLICY_FIFO ? (uint32_t)cand_pos(u) : __float_as_uint(score[u]);
                 ebits[u] = eb;
                 lo = min(lo, eb);
                 hi = max(hi, eb);
@@ -910,6 +1016,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
             const int slot = i < nFr ? freed[i] : cnt + (i - nFr);
             cref[slot] = xE0 + (u - cnt);
             cpos[slot] = (int)(eS + (u - cnt));
+            cscoreL[slot] = score[u];
         }
         cnt = nU < C ? nU : C;
         __syncthreads();
@@ -922,7 +1029,10 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         *(float4*)(Hd + (size_t)(wave * 16 + r16) * F + ft * 16 + qg * 4) =
             make_float4(Hr[ft][0], Hr[ft][1], Hr[ft][2], Hr[ft][3]);
     for (int i = tid; i < F; i += NT) ch.s()[i] = sP[perm_pos(i)];
-    for (int i = tid; i < cnt; i += NT) ch.cpos()[i] = cpos[i];
+    for (int i = tid; i < cnt; i += NT) {
+        ch.cpos()[i] = cpos[i];
+        ch.cscore()[i] = cscoreL[i];
+    }
     // cache and window rows in 16-byte pieces
     constexpr int EP = 16 / (int)sizeof(T), NP = D / EP;
     static_assert(D % EP == 0, "rows are whole 16-byte pieces");

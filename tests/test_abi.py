@@ -87,3 +87,16 @@ def test_bad_arguments_rejected_before_launch():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lola.status_string(s), str) and lola.status_string(s)
+
+
+def test_policy_checks():
+    """Policies outside the enum are rejected; lola_decode_step takes only the SRE policy."""
+    lib = lola.lib()
+    fake = ctypes.c_void_p(4096)
+    bad = I.LayerConfig(4, 2, 64, 32, 8, 8, 8, "f32", policy=7)
+    assert lola.state_bytes(bad, 1) == 0
+    for p in (1, 2, 3, 4):
+        layer = I.LayerConfig(4, 2, 64, 32, 8, 8, 8, "f32", policy=p)
+        assert lola.state_bytes(layer, 1) > 0
+        rc = lib.lola_decode_step(ctypes.byref(lola.config(layer)), fake, 1, fake, fake, fake, fake, None)
+        assert rc == -2
