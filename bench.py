@@ -188,9 +188,8 @@ def bench_prefill(wl, steps, warmup):
     return cold
 
 
-def bench_decode(wl, steps_timed, warmup):
-    """64 sequences: 4096-token prefill (untimed) then `steps_timed` decode steps."""
-    L = wl.layer
+def decode_state(wl, layer):
+    """The decode workload's 64 states after their 4096-token prefill (outputs unused)."""
     B, T = wl.batch, wl.seq_len
     Ks, Vs = [], []
     W = None
@@ -200,52 +199,77 @@ def bench_decode(wl, steps_timed, warmup):
             W = Wb
         Ks.append(K)
         Vs.append(V)
-    Wd = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(W, (L.n_kv_heads,) + W.shape))).to("cuda")
-    k = to_dev(np.stack(Ks), L)
-    v = to_dev(np.stack(Vs), L)
+    Wd = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(W, (layer.n_kv_heads,) + W.shape))).to("cuda")
+    k = to_dev(np.stack(Ks), layer)
+    v = to_dev(np.stack(Vs), layer)
     del Ks, Vs
-    q = torch.zeros((B, T, L.n_q_heads, L.head_dim), dtype=k.dtype, device="cuda")  # outputs unused here
-    state = lola.init_state(L, B, Wd)
-    lola.prefill(L, state, q, k, v)
+    q = torch.zeros((B, T, layer.n_q_heads, layer.head_dim), dtype=k.dtype, device="cuda")
+    state = lola.init_state(layer, B, Wd)
+    lola.prefill(layer, state, q, k, v)
     del q, k, v
-    require_healthy(L, [state], B, "decode prefill")
-    qd, kd, vd = I.make_decode_steps(wl, steps_timed)
-    qd, kd, vd = to_dev(qd, L), to_dev(kd, L), to_dev(vd, L)
+    require_healthy(layer, [state], B, "decode prefill")
+    return state
+
+
+def time_decode(layer, state, B, qd, kd, vd, warmup):
+    """Mean per-step time (us) of decode steps from `state`, cold and warm.  Cold: a 512 MiB
+    buffer is rewritten before each step, outside its events, so each step reads the
+    state from HBM; warm: no flush.  Per-step HIP events on the launch stream."""
+    steps = qd.shape[0]
     outd = torch.empty_like(qd[0])
-    base = state.clone()
     warm_state = state.clone()
     for s in range(warmup):
-        lola.decode(L, warm_state, qd[s], kd[s], vd[s], out=outd)
+        lola.decode(layer, warm_state, qd[s], kd[s], vd[s], out=outd)
     torch.cuda.synchronize()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
     def timed(st, cold):
-        """Per-step events; cold: the 512 MiB buffer is rewritten before each step,
-        outside its events, so each step reads the state from HBM."""
-        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps_timed)]
-        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps_timed)]
-        for s in range(steps_timed):
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for s in range(steps):
             if cold:
                 flush.fill_(s & 0xFF)
             e0[s].record()
-            lola.decode(L, st, qd[s], kd[s], vd[s], out=outd)
+            lola.decode(layer, st, qd[s], kd[s], vd[s], out=outd)
             e1[s].record()
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1000.0
 
-    cold_state = base.clone()
+    cold_state = state.clone()
     us_cold = timed(cold_state, True)
     us_warm = timed(state, False)
-    require_healthy(L, [cold_state, state, warm_state], B, "decode")
-    del cold_state, warm_state, base, flush
+    require_healthy(layer, [cold_state, state, warm_state], B, "decode")
+    return us_cold, us_warm
+
+
+def bench_decode(wl, steps_timed, warmup):
+    """64 sequences: 4096-token prefill (untimed) then `steps_timed` decode steps; the same
+    with the incremental decode scores (fewer steps) for comparison."""
+    L = wl.layer
+    B = wl.batch
+    state = decode_state(wl, L)
+    qd, kd, vd = I.make_decode_steps(wl, steps_timed)
+    qd, kd, vd = to_dev(qd, L), to_dev(kd, L), to_dev(vd, L)
+    us_cold, us_warm = time_decode(L, state, B, qd, kd, vd, warmup)
     nbytes = decode_bytes(L, B)
 
-    def roof(us):
-        gbs = nbytes / (us * 1e-6) / 1e9
+    def roof(us, nb=nbytes):
+        gbs = nb / (us * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "bytes_per_launch": nbytes, "traffic": measured_traffic("decode")}
+                "bytes_per_launch": nb, "traffic": measured_traffic("decode")}
 
     mixed = bench_mixed(wl, state)
+    del state
+    # incremental decode scores (stored n, d per cached pair): the first step after the
+    # prefill recomputes them, so it is one of the untimed warm-up steps
+    Li = I.LayerConfig(L.n_q_heads, L.n_kv_heads, L.head_dim, L.feat_half, L.window, L.cache_cap, L.chunk,
+                       L.io_dtype, L.softmax_scale, L.policy, 1)
+    st_i = decode_state(wl, Li)
+    n_i = min(steps_timed, 64)
+    lola.decode(Li, st_i, qd[-1], kd[-1], vd[-1])  # the full recomputation, untimed
+    ic, iw = time_decode(Li, st_i, B, qd[:n_i], kd[:n_i], vd[:n_i], warmup)
+    del st_i
+    nb_i = nbytes + B * L.n_kv_heads * 2 * L.cache_cap * (L.head_dim + 1) * 4  # stored n, d read and written
     return {
         "workload": wl.name,
         "value": B / (us_cold * 1e-6),
@@ -254,6 +278,9 @@ def bench_decode(wl, steps_timed, warmup):
         "timing": "cold (512 MiB rewritten before each step, outside its events), per-step HIP events",
         "roofline": roof(us_cold),
         "warm": {"value": B / (us_warm * 1e-6), "us_per_step": us_warm, "roofline": roof(us_warm)},
+        "incremental_scores": {"us_per_step": ic, "value": B / (ic * 1e-6), "steps": n_i,
+                               "warm": {"us_per_step": iw, "value": B / (iw * 1e-6)},
+                               "bytes_per_launch": nb_i, "roofline": roof(ic, nb_i)},
         "mixed": mixed,
     }
 

@@ -100,6 +100,21 @@ typedef enum { LOLA_F32 = 0, LOLA_BF16 = 1 } lola_dtype;
  * lola_prefill_ragged (any token count, so n_tokens = 1 gives the token-by-
  * token mode); lola_decode_step's fused kernel implements LOLA_POLICY_SRE only
  * and returns LOLA_ERR_UNSUPPORTED for the others. */
+/* How lola_decode_step scores the cached pairs (same result, other cost):
+ *   LOLA_DECODE_RESCORE      every step computes H^T phi(k) and s . phi(k) for
+ *                            every cached pair against the step-start state (the
+ *                            summary's "Inferentiestrategie", step 1, as written)
+ *   LOLA_DECODE_INCREMENTAL  the state keeps, per cached pair, n = H^T phi(k) and
+ *                            d = s . phi(k); a step scores the cache from them and
+ *                            adds the one folded pair's share, (phi(k) . phi(k_f))
+ *                            times [v_f; 1], instead of recomputing them: O(C (F + D))
+ *                            work per step instead of O(C F D), against 4 (D + 1)
+ *                            more bytes of state per cached pair read and written.
+ *                            bf16 io and LOLA_POLICY_SRE only.  A prefill call
+ *                            marks the stored n, d stale; the next decode step
+ *                            recomputes them in full. */
+typedef enum { LOLA_DECODE_RESCORE = 0, LOLA_DECODE_INCREMENTAL = 1 } lola_decode_mode;
+
 typedef enum {
     LOLA_POLICY_SRE = 0,
     LOLA_POLICY_SRE_STALE = 1,
@@ -119,6 +134,7 @@ typedef struct {
     int32_t io_dtype;      /* lola_dtype */
     float softmax_scale;   /* tau on q.k; <= 0 selects 1/sqrt(head_dim) */
     int32_t policy;        /* one of lola_policy; 0 = the SRE of the method */
+    int32_t decode_mode;   /* one of lola_decode_mode; 0 = rescore every cached pair */
 } lola_config;
 
 /* Bytes of the state buffer for `batch` sequences: a header, W, and per

@@ -68,6 +68,10 @@ lola_status make_dims(const lola_config* cfg, Dims* d)
     if (cfg->io_dtype != LOLA_F32 && cfg->io_dtype != LOLA_BF16) return LOLA_ERR_UNSUPPORTED;
     if (!(cfg->softmax_scale == cfg->softmax_scale)) return LOLA_ERR_INVALID_ARG;  // NaN
     if (cfg->policy < LOLA_POLICY_SRE || cfg->policy > LOLA_POLICY_SOFTMAX_ERR) return LOLA_ERR_UNSUPPORTED;
+    if (cfg->decode_mode != LOLA_DECODE_RESCORE && cfg->decode_mode != LOLA_DECODE_INCREMENTAL)
+        return LOLA_ERR_UNSUPPORTED;
+    if (cfg->decode_mode == LOLA_DECODE_INCREMENTAL && (cfg->io_dtype != LOLA_BF16 || cfg->policy != LOLA_POLICY_SRE))
+        return LOLA_ERR_UNSUPPORTED;
     d->Hq = cfg->n_q_heads;
     d->Hkv = cfg->n_kv_heads;
     d->D = cfg->head_dim;
@@ -81,6 +85,7 @@ lola_status make_dims(const lola_config* cfg, Dims* d)
     d->esize = cfg->io_dtype == LOLA_BF16 ? 2 : 4;
     d->tau = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
     d->policy = cfg->policy;
+    d->inc = cfg->decode_mode == LOLA_DECODE_INCREMENTAL ? 1 : 0;
     return LOLA_OK;
 }
 
@@ -99,6 +104,7 @@ uint64_t cfg_hash(const lola_config* c, int batch)
     mix((uint32_t)c->feat_half); mix((uint32_t)c->window); mix((uint32_t)c->cache_cap);
     mix((uint32_t)c->chunk); mix((uint32_t)c->io_dtype); mix(sc); mix((uint32_t)batch);
     if (c->policy != 0) mix(0x9e3779b9u ^ (uint32_t)c->policy);
+    if (c->decode_mode != 0) mix(0x85ebca6bu ^ (uint32_t)c->decode_mode);
     return h;
 }
 
@@ -210,8 +216,13 @@ lola_status launch_decode(Args& a, hipStream_t s)
 {
     if constexpr (sizeof(T) == 2) {
         const size_t lds = dec_smem<D, F>(a.d.C).total;
-        if (allow_lds(decode_kernel_bf16<D, F>, lds) != hipSuccess) return LOLA_ERR_HIP;
-        hipLaunchKernelGGL((decode_kernel_bf16<D, F>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+        if (a.d.inc) {
+            if (allow_lds(decode_kernel_bf16<D, F, true>, lds) != hipSuccess) return LOLA_ERR_HIP;
+            hipLaunchKernelGGL((decode_kernel_bf16<D, F, true>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+            return hip_status(hipGetLastError());
+        }
+        if (allow_lds(decode_kernel_bf16<D, F, false>, lds) != hipSuccess) return LOLA_ERR_HIP;
+        hipLaunchKernelGGL((decode_kernel_bf16<D, F, false>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
     } else {
         const size_t lds = decode_smem(D, F, a.d.G, a.d.C).total;
         if (allow_lds(decode_kernel<D, F, T>, lds) != hipSuccess) return LOLA_ERR_HIP;

@@ -30,7 +30,7 @@ namespace lola {
 constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
 
 struct DecSmem {
-    size_t HhT, HlT, Wl, sP, cposL, esc, phiE, phiF, xrow, stVT, misc, total;
+    size_t HhT, HlT, Wl, sP, cposL, esc, phiE, phiF, xrow, stVT, nE, phiFop, misc, total;
 };
 
 // The two arrays sized by the cache capacity come last: every other offset is a
@@ -49,6 +49,8 @@ __host__ __device__ constexpr DecSmem dec_smem(int C)
     m.phiF = off;  off += align_up(sizeof(float) * F, 16);
     m.xrow = off;  off += align_up(sizeof(float) * D, 16);
     m.stVT = off;  off += align_up(sizeof(uint16_t) * (size_t)D * (kDecBlock + 8), 16);
+    m.nE = off;    off += align_up(sizeof(float) * (D + 4), 16);   // incremental decode: n, d of the leaving key
+    m.phiFop = off; off += align_up(sizeof(float) * F, 16);       // incremental decode: folded phi, operand order
     m.misc = off;  off += align_up(sizeof(int) * 16, 16);
     m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
     m.esc = off;   off += align_up(sizeof(float) * (size_t)(Cp + 1), 16);
@@ -129,7 +131,7 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
 // feature index of operand slot h (see phi_tile) for lane group qg
 __device__ __forceinline__ int slot_feature(int h, int qg) { return (2 * (h >> 3) + ((h & 7) >> 2)) * 16 + qg * 4 + (h & 3); }
 
-template <int D, int F>
+template <int D, int F, bool INC>
 __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
 {
     constexpr int NW = 4, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
@@ -152,12 +154,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     uint16_t* stVT = (uint16_t*)(smem + sm.stVT);
     int* misc = (int*)(smem + sm.misc);
     float* mrg = (float*)(smem + sm.stVT);  // merge area, reused after the key loop
+    float* nEL = (float*)(smem + sm.nE);    // incremental decode: n of the leaving key, then d at [D]
+    float* phiFop = (float*)(smem + sm.phiFop);
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
     Chain ch = chain_of(a, chain);
     const int64_t t = ch.tok();
     const int cnt = min(max(ch.cnt(), 0), C);
+    // incremental decode: the stored n = H^T phi(k), d = s . phi(k) of the cached pairs
+    // match the state (a prefill call marks them stale)
+    const bool incValid = INC && ch.incv() == 1;
     const bf16* knew = (const bf16*)a.k + ((size_t)b * d.Hkv + g) * D;
     const bf16* vnew = (const bf16*)a.v + ((size_t)b * d.Hkv + g) * D;
     const bool hasE = (w == 0) || (t - w >= 0);
@@ -235,8 +242,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     // in hi/lo parts (hi.hi + lo.hi + hi.lo; the H operands are read once for all P
     // tiles), e = |n / d - v|^2 (values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p]
     // whether the column is a candidate)
+    // (nout[p], if given, receives candidate r16's n at its rows dt * 16 + 4 qg .. + 3)
     auto sre_core = [&](auto pTag, const bf16x8 (*bh)[FM], const bf16x8 (*bl)[FM], const float* inv, const bool* cv,
-                        const uint2 (*vq)[DT], float* e) {
+                        const uint2 (*vq)[DT], float* e, float* const* nout = nullptr) {
         constexpr int P = decltype(pTag)::value;
         float es[P];
 #pragma unroll
@@ -267,6 +275,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                     const float df = (acc[p][i] + acc2[p][i]) * inv[p] - (cv[p] ? vv[i] : 0.f);
                     es[p] += df * df;
                 }
+                if (nout && nout[p])
+                    *(float4*)(nout[p] + dt * 16 + qg * 4) = make_float4(acc[p][0] + acc2[p][0], acc[p][1] + acc2[p][1],
+                                                                         acc[p][2] + acc2[p][2], acc[p][3] + acc2[p][3]);
             }
         }
 #pragma unroll
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     };
     // 1 / d with d = s . (phi hi + phi lo): the feature values the MFMAs see (the
     // prefill scan scores with the same 16-bit features)
-    auto inv_d = [&](const bf16x8* bh, const bf16x8* bl) -> float {
+    auto dot_s = [&](const bf16x8* bh, const bf16x8* bl) -> float {
         float dd = 0.f;
 #pragma unroll
         for (int mf = 0; mf < FM; ++mf) {
@@ -285,12 +296,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) dd += (bf16_val(uh[j]) + bf16_val(ul[j])) * sP[mf * 32 + qg * 8 + j];
         }
-        dd = quad_sum(dd);
+        return quad_sum(dd);
+    };
+    auto inv_d = [&](const bf16x8* bh, const bf16x8* bl) -> float {
+        const float dd = dot_s(bh, bl);
         return dd > 0.f ? 1.f / dd : 0.f;
     };
     // SRE of P tiles whose features are computed here from the key fragments kb[p]
     auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
-                         float* phi0 = nullptr) {  // phi0: phi of candidate 0 of tile 0, natural order
+                         float* phi0 = nullptr,    // phi0: phi of candidate 0 of tile 0, natural order
+                         float* nd0 = nullptr) {   // nd0: n (D values) then d of candidate 0 of tile 0
         constexpr int P = decltype(pTag)::value;
         bf16x8 bh[P][FM], bl[P][FM];
         float inv[P];
@@ -315,10 +330,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                     bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
                     bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
                 }
-                inv[p] = inv_d(bh[p], bl[p]);
+                const float dd = dot_s(bh[p], bl[p]);
+                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
+                if (nd0 && p == 0 && lane == 0) nd0[D] = dd;
             }
         }
-        sre_core(pTag, bh, bl, inv, cv, vq, e);
+        float* nout[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) nout[p] = (nd0 && p == 0 && r16 == 0) ? nd0 : nullptr;
+        sre_core(pTag, bh, bl, inv, cv, vq, e, nout);
     };
 
     // Wave 3: phi of the leaving key (column 0 of a tile) and, when a pair must be
@@ -336,13 +356,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         bf16x8 kb[1][DS];
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) kb[0][ks] = __builtin_bit_cast(bf16x8, kEq[ks]);
-        if (hasE && nU > C) {
+        if (hasE && (nU > C || INC)) {  // (incremental decode: n, d of a key that may enter the cache)
             const bool cv[1] = {r16 == 0};
             uint2 vq[1][DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vq[0][dt] = vEq[dt];
             float e[1];
-            sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vq, e, phiE);
+            sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vq, e, phiE, INC ? nEL : nullptr);
             if (lane == 0) esc[cnt] = e[0];
         } else {
             float x[1][F / 4];
@@ -545,7 +565,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
 
-    const bool scoreCache = hasE && nU > C;  // the SRE pass over the cache runs
+    // the MFMA SRE pass over the cache runs: to choose a victim, or (incremental decode)
+    // to compute the stored n, d of every cached pair afresh; otherwise the incremental
+    // decode scores a full cache from the stored n, d
+    const bool scoreCache = INC ? (!incValid && cnt > 0) : (hasE && nU > C);
+    const bool storedScores = INC && incValid && hasE && nU > C;
     const int nT = (cnt + 15) / 16;
     // features of the cached keys come from the state (hi | lo rows in operand order)
     uint4 fq[2][2 * FM];
@@ -602,7 +626,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     //      pair's was scored with its phi): the cache in tiles of 16 slots dealt to
     //      the waves in turn; each tile's key and value rows are loaded while the
     //      previous tiles are scored ----
-    if (hasE && nU > C) {
+    if (scoreCache) {
         for (int t0 = wave; t0 < nT; t0 += 2 * NW) {
             const int tl[2] = {t0, t0 + NW};
             bf16x8 bh[2][FM], bl[2][FM];
@@ -622,14 +646,52 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             }
             if (t0 + 2 * NW < nT) tile_load(0, t0 + 2 * NW);
             if (t0 + 3 * NW < nT) tile_load(1, t0 + 3 * NW);
+            float* nout[2] = {nullptr, nullptr};
 #pragma unroll
-            for (int p = 0; p < 2; ++p) inv[p] = inv_d(bh[p], bl[p]);
+            for (int p = 0; p < 2; ++p) {
+                const float dd = dot_s(bh[p], bl[p]);
+                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
+                if (INC && cv[p]) {  // the stored n, d of this cached pair, computed afresh
+                    const int slot = tl[p] * 16 + r16;
+                    nout[p] = ch.cn() + (size_t)slot * D;
+                    if (qg == 0) ch.cd()[slot] = dd;
+                }
+            }
             float e[2];
-            if (tl[1] < nT) sre_core(std::integral_constant<int, 2>{}, bh, bl, inv, cv, vv, e);  // wave-uniform
-            else sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, cv, vv, e);
+            if (tl[1] < nT) sre_core(std::integral_constant<int, 2>{}, bh, bl, inv, cv, vv, e, nout);  // wave-uniform
+            else sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, cv, vv, e, nout);
 #pragma unroll
             for (int p = 0; p < 2; ++p)
                 if (tl[p] < nT && qg == 0 && cv[p]) esc[tl[p] * 16 + r16] = e[p];
+        }
+    }
+    if constexpr (INC) {
+        if (storedScores) {
+            // e = |n / d - v|^2 from the stored n, d: 16 lanes per cached pair, D / 16
+            // values each (one 16-lane group reads a contiguous row)
+            constexpr int DPL = D / 16;
+            const int sub = lane & 15;
+            for (int u = (tid >> 4); u < cnt; u += 16) {
+                const float dd = ch.cd()[u];
+                const float inv = dd > 0.f ? 1.f / dd : 0.f;
+                const float* nr = ch.cn() + (size_t)u * D + sub * DPL;
+                const bf16* vr = ch.cache_v<bf16>() + (size_t)u * D + sub * DPL;
+                float e = 0.f;
+#pragma unroll
+                for (int j = 0; j < DPL; j += 4) {
+                    float nv[4], vv[4];
+                    load4(nr + j, nv);
+                    load4(vr + j, vv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float df = nv[i] * inv - vv[i];
+                        e += df * df;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
+                if (sub == 0) esc[u] = e;
+            }
         }
     }
     __syncthreads();
@@ -671,9 +733,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 for (int f = lane; f < F; f += 64) {
                     const int q = perm_pos(f);
                     phiF[f] = bf16_val(pr[q]) + bf16_val(pr[F + q]);
+                    if (INC) phiFop[q] = phiF[f];
                 }
             } else
-                for (int f = lane; f < F; f += 64) phiF[f] = phiE[f];
+                for (int f = lane; f < F; f += 64) {
+                    phiF[f] = phiE[f];
+                    if (INC) phiFop[perm_pos(f)] = phiE[f];
+                }
         } else if (wave == 1) {
             const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
             for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
@@ -690,6 +756,58 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             *(float4*)(Hd + i) = h4[k];
         }
         for (int f = tid; f < F; f += 256) ch.s()[f] += phiF[f];
+    }
+
+    if constexpr (INC) {
+        // ---- stored n, d after this step: every cached pair that stays gains the folded
+        //      pair's share, kappa = phi(k) . phi(k_f) times [v_f; 1] (H += phi_f v_f^T and
+        //      s += phi_f leave n = H^T phi(k), d = s . phi(k) exactly that much larger);
+        //      a leaving key that enters the cache brings its own n, d (wave 3 computed
+        //      them against the step-start state) plus its share of the fold ----
+        const bool folded = hasE && nU > C;
+        if (folded) {
+            constexpr int PPL = F / 16, DPL = D / 16;
+            const int sub = lane & 15;
+            for (int u = (tid >> 4); u < cnt; u += 16) {
+                if (u == victim) continue;  // (the whole 16-lane group)
+                const uint16_t* pr = ch.cphi() + (size_t)u * 2 * F + sub * PPL;
+                float kk = 0.f;
+#pragma unroll
+                for (int j = 0; j < PPL; j += 4) {
+                    const uint2 h2 = *(const uint2*)(pr + j), l2 = *(const uint2*)(pr + F + j);
+                    const uint32_t hw[2] = {h2.x, h2.y}, lw[2] = {l2.x, l2.y};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float hv = __uint_as_float((i & 1) ? (hw[i >> 1] & 0xffff0000u) : (hw[i >> 1] << 16));
+                        const float lv = __uint_as_float((i & 1) ? (lw[i >> 1] & 0xffff0000u) : (lw[i >> 1] << 16));
+                        kk += (hv + lv) * phiFop[sub * PPL + j + i];
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) kk += __shfl_xor(kk, o, 64);
+                float* nr = ch.cn() + (size_t)u * D + sub * DPL;
+#pragma unroll
+                for (int j = 0; j < DPL; j += 4) {
+                    float4 n4 = *(const float4*)(nr + j);
+                    n4.x += kk * xrow[sub * DPL + j];
+                    n4.y += kk * xrow[sub * DPL + j + 1];
+                    n4.z += kk * xrow[sub * DPL + j + 2];
+                    n4.w += kk * xrow[sub * DPL + j + 3];
+                    *(float4*)(nr + j) = n4;
+                }
+                if (sub == 0) ch.cd()[u] += kk;
+            }
+        }
+        const int enter = !hasE ? -1 : (nU <= C ? cnt : (victim < cnt ? victim : -1));
+        if (enter >= 0 && wave == 0) {
+            float ke = 0.f;
+            if (folded) {
+                for (int f = lane; f < F; f += 64) ke += phiE[f] * phiF[f];
+                ke = wave_sum(ke);
+            }
+            for (int j = lane; j < D; j += 64) ch.cn()[(size_t)enter * D + j] = nEL[j] + (folded ? ke * xrow[j] : 0.f);
+            if (lane == 0) ch.cd()[enter] = nEL[D] + ke;
+        }
     }
 
     // ---- cache slot, then the ring (the leaving pair lives in slot t % w) ----
@@ -723,6 +841,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         if (slot >= 0) ch.cpos()[slot] = (int32_t)pE;
         if (hasE && nU <= C) ch.cnt() = cnt + 1;
         ch.tok() = t + 1;
+        if (INC) ch.incv() = 1;
     }
 }
 

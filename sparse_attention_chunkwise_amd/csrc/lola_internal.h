@@ -60,6 +60,7 @@ struct Dims {
     int esize;    // bytes per io element
     float tau;    // softmax scale on q.k
     int policy;   // lola_policy
+    int inc;      // 1: the state keeps n = H^T phi(k), d = s . phi(k) per cached pair (incremental decode)
 };
 
 struct StateHeader {
@@ -78,13 +79,16 @@ static_assert(sizeof(StateHeader) == 32, "kernels test the first 32 bytes of a s
 //        cache_phi [C][2F] bf16 (bf16 io only: phi of each cached key as hi and lo parts,
 //        each in MFMA operand order, so that a decode step scores the cache without
 //        recomputing the feature map) | cache_score [C] f32 (the score each cached
-//        pair was kept with; the stale-score policy reads it back)
+//        pair was kept with; the stale-score policy reads it back) |
+//        incremental decode only: cache_n [C][D] f32 (H^T phi(k) of each cached pair),
+//        cache_d [C] f32 (s . phi(k)); the int32 at chain offset 12 is 1 while they
+//        match the state (a prefill call sets it to 0)
 // Every chain keeps its own token count so that concurrent chains of one
 // sequence never race on a shared counter.  The window ring slot of
 // position p is p % w.
 struct StateLayout {
     size_t W, Wb, chains, chain_bytes;
-    size_t otok, ocnt, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi, oscore;
+    size_t otok, ocnt, oincv, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi, oscore, ocn, ocd;
     size_t total;
 };
 
@@ -99,7 +103,8 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     s.chains = off;
     size_t c = 0;
     s.otok = 0;
-    s.ocnt = 8;      c = 256;
+    s.ocnt = 8;
+    s.oincv = 12;    c = 256;
     s.oH = c;        c = align_up(c + sizeof(float) * (size_t)d.F * d.D, 256);
     s.os = c;        c = align_up(c + sizeof(float) * (size_t)d.F, 256);
     s.ocpos = c;     c = align_up(c + sizeof(int32_t) * (size_t)(d.C > 0 ? d.C : 1), 256);
@@ -109,6 +114,8 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     s.ocache_v = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
     s.ocphi = c;     c = align_up(c + (d.io == 1 ? sizeof(uint16_t) * 2 * (size_t)d.F * d.C : 0), 256);
     s.oscore = c;    c = align_up(c + sizeof(float) * (size_t)(d.C > 0 ? d.C : 1), 256);
+    s.ocn = c;       c = align_up(c + (d.inc ? sizeof(float) * (size_t)d.C * d.D : 0), 256);
+    s.ocd = c;       c = align_up(c + (d.inc ? sizeof(float) * (size_t)d.C : 0), 256);
     s.chain_bytes = c;
     s.total = s.chains + c * (size_t)B * d.Hkv;
     return s;

@@ -43,6 +43,9 @@ struct Chain {
     template <typename T> __device__ T* cache_v() const { return (T*)(base + sl->ocache_v); }
     __device__ uint16_t* cphi() const { return (uint16_t*)(base + sl->ocphi); }  // bf16 io
     __device__ float* cscore() const { return (float*)(base + sl->oscore); }
+    __device__ int32_t& incv() const { return *(int32_t*)(base + sl->oincv); }  // incremental n, d valid
+    __device__ float* cn() const { return (float*)(base + sl->ocn); }           // [C][D]
+    __device__ float* cd() const { return (float*)(base + sl->ocd); }           // [C]
 };
 
 __device__ __forceinline__ Chain chain_of(const Args& a, int chain)
@@ -1069,6 +1072,7 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
     if (tid == 0) {
         ch.cnt() = cnt;
         ch.tok() = t0 + ns;
+        ch.incv() = 0;  // stored incremental decode scores no longer match
     }
 }
 

@@ -956,6 +956,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
     if (tid == 0) {
         ch.cnt() = cnt;
         ch.tok() = t0 + ns;
+        ch.incv() = 0;  // stored incremental decode scores no longer match
     }
 }
 

@@ -45,6 +45,7 @@ class LayerConfig:
     io_dtype: str  # "f32" or "bf16"
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(head_dim)
     policy: int = 0  # scoring / cache policy: 0 SRE, 1 stale SRE (min-heap), 2 FIFO, 3 attention weight, 4 softmax error
+    decode_mode: int = 0  # 0 decode steps rescore the cache, 1 they update stored scores (same result)
 
     @property
     def feat_dim(self) -> int:

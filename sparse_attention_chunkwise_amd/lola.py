@@ -37,7 +37,7 @@ class LolaConfig(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("feat_half", ctypes.c_int32), ("window", ctypes.c_int32), ("cache_cap", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("policy", ctypes.c_int32)]
+                ("policy", ctypes.c_int32), ("decode_mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,7 +86,8 @@ def config(layer) -> LolaConfig:
     """C config from a LayerConfig-like object (inputs.LayerConfig)."""
     io = BF16 if layer.io_dtype == "bf16" else F32
     return LolaConfig(layer.n_q_heads, layer.n_kv_heads, layer.head_dim, layer.feat_half, layer.window,
-                      layer.cache_cap, layer.chunk, io, float(layer.softmax_scale), int(layer.policy))
+                      layer.cache_cap, layer.chunk, io, float(layer.softmax_scale), int(layer.policy),
+                      int(getattr(layer, "decode_mode", 0)))
 
 
 def torch_dtype(layer):
