@@ -1,15 +1,18 @@
 // Output pass for bf16 io (gfx950), LDS-staged.
 //
-// One workgroup (8 waves) handles 128 query rows of one (interval, chain);
-// each wave owns 16 rows as one 16-column MFMA tile (the queries are the
-// columns, so softmax statistics live in the lanes).  Per workgroup:
+// One workgroup (8 waves) handles 256 query rows of one (interval, chain) --
+// all G * L of them at the 4K workload's shapes, so the window, cache and
+// snapshot tiles of an interval are staged once; each wave owns 32 rows as two
+// 16-column MFMA tiles (the queries are the columns, so softmax statistics live
+// in the lanes), and every K, V and phi(K) operand read from LDS feeds both
+// tiles.  Per workgroup:
 //   - H_c^T (bf16, features in operand order) and W (bf16 hi + lo) staged in LDS
 //     once (every load issued before any is waited for);
 //   - z^T = W Q^T gives phi(q) (two softmax halves over the features),
 //     O^T = H_c^T phi(q)^T and Z = s_c . phi(q) start the accumulators
 //     (linear read of the interval-start state, LoLA summary section
 //     "Inferentiestrategie", step 4);
-//   - keys in blocks of 64 (the window span of the interval, then the cache
+//   - keys in blocks of 32 (the window span of the interval, then the cache
 //     snapshot): K, V^T and phi(K) are staged in LDS with 16-byte loads, the
 //     next block prefetched into registers; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
 //     for keys that left the window inside the interval, online softmax with
@@ -22,9 +25,9 @@
 
 namespace lola {
 
-constexpr int kOutRows = 128;  // query rows per workgroup
-constexpr int kKeyBlock = 64;
-constexpr int kOutThreads = 512;  // 8 waves x 16 query rows
+constexpr int kOutRows = 256;  // query rows per workgroup
+constexpr int kKeyBlock = 32;  // (two row tiles per wave with 64-key blocks spill registers)
+constexpr int kOutThreads = 512;  // 8 waves x 32 query rows
 
 struct OutSmem {
     size_t sP, refs, Wl, Hs, Ks, VT, Pk, rowK, rowV, total;
@@ -55,7 +58,7 @@ __device__ __forceinline__ int key_perm(int k) { return ((k & 15) >> 2) * 8 + (k
 template <int D, int F>
 __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 {
-    constexpr int NT = kOutThreads, NW = NT / 64, RT = 1, KB = kKeyBlock, Fh = F / 2, FM = F / 32, DS = D / 32,
+    constexpr int NT = kOutThreads, NW = NT / 64, RT = 2, KB = kKeyBlock, Fh = F / 2, FM = F / 32, DS = D / 32,
                   DT = D / 16;
     constexpr int KP = D + 8, VP = KB + 8, PP = F + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
