@@ -393,12 +393,13 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
         const int T = (nU + 15) / 16;
 
         // ---- interval-start snapshot: H^T hi parts of this block's rows, s and cache
-        //      refs (written before the fold and the selection change them) ----
+        //      refs (written before the fold and the slot update change them) ----
         // (the blocks of a column slice hold identical rows, and every block the
         // same s and slot codes, so the writes are spread: block ju writes the
-        // 32-feature pieces m with m % PU == ju, two other blocks s and the refs)
-        auto snapshot = [&]() {
-            if (wave == 0) {
+        // 32-feature pieces m with m % PU == ju, two other blocks s and the refs).
+        // Threads t0 .. NT - 1 write it: waves 1.. while wave 0 selects, or all.
+        auto snapshot = [&](int t0) {
+            if (wave == 1) {
                 uint16_t* dst = (uint16_t*)(a.ws + a.wl.snapH) + ((size_t)chain * NI + c) * F * D +
                                 (size_t)(col0 + r16) * F + qg * 8;
 #pragma unroll
@@ -407,12 +408,12 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             }
             if (jw == 1 % KW && ju == (1 & (PU - 1))) {
                 float* snapS = (float*)(a.ws + a.wl.snapS) + ((size_t)chain * NI + c) * F;
-                for (int i = tid; i < F; i += NT) snapS[i] = sP[perm_pos(i)];
+                for (int i = tid - t0; i < F; i += NT - t0) snapS[i] = sP[perm_pos(i)];
             }
             if (jw == 2 % KW && ju == (2 & (PU - 1))) {
                 int* snapRef = (int*)(a.ws + a.wl.snapRef) + ((size_t)chain * NI + c) * Cp;
-                for (int i = tid; i < cnt; i += NT) snapRef[i] = cref[i];
-                if (tid == 0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
+                for (int i = tid - t0; i < cnt; i += NT - t0) snapRef[i] = cref[i];
+                if (tid == t0) ((int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c] = cnt;
             }
         };
 
@@ -440,7 +441,6 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     }
             }
             ++arrivals;
-            snapshot();  // overlaps the wait for the other blocks' partials
 
             // ---- SRE totals: every block's partial, added in column-slice order
             //      (the same bits in every block); a slot is read again until it
@@ -463,8 +463,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                     for (int jj = 0; jj < KW; ++jj)
                         ready &= (uint32_t)(va[jj] >> 32) == tag && (uint32_t)(vb[jj] >> 32) == tag;
                     if (ready) break;
-                    if (++polls > kSpinLimit ||
-                        __hip_atomic_load(&xsync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                    // the give-up flag costs a round trip of its own: it is read every
+                    // 64th pass only
+                    if ((++polls & 63u) == 0u &&
+                        (polls > kSpinLimit ||
+                         __hip_atomic_load(&xsync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
                         ok = 0;
                         break;
                     }
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             lds_sync();
             if (misc[8] == (int)tag) return;  // block-uniform
         } else
-            snapshot();
+            snapshot(0);
 
         // ---- wave 0: exact top-C on (SRE desc, position asc), compaction, slot
         //      updates and the next interval's candidate list ----
@@ -537,13 +540,21 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 int ucv[NC];              // candidate codes
                 uint64_t km[NC], vm[NC];  // keep and valid masks per chunk
                 // (both arrays hold at least 64 NC entries: the loads need no branch)
+                uint32_t eb[NC];
+                int cr[NC];
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    eb[i] = ebits[i * 64 + lane];
+                    cr[i] = cref[i * 64 + lane];
+                }
+                // (all ten reads issued before the first wait)
+#pragma unroll
+                for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(eb[i]), "+v"(cr[i]));
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
                     const int u = i * 64 + lane;
-                    const uint32_t eb = ebits[u];
-                    const int cr = cref[u];
-                    key[i] = (needSel && u < nU) ? eb : 0u;
-                    ucv[i] = u < cnt ? cr : xE0 + (u - cnt);
+                    key[i] = u < nU ? eb[i] : 0u;
+                    ucv[i] = u < cnt ? cr[i] : xE0 + (u - cnt);
                     vm[i] = __ballot(u < nU);
                     km[i] = (!needSel && nU <= C) ? vm[i] : 0ull;
                 }
@@ -760,8 +771,10 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
             if (nch <= 2) select_compact(std::integral_constant<int, 2>{});
             else if (nch <= 5) select_compact(std::integral_constant<int, 5>{});
             else select_wide();
-        } else
+        } else {
             prefetch_new(nUN, cntN, ivN.xE0);
+            if (needSel) snapshot(64);
+        }
         lds_sync();
         const int nF = misc[5];
 
