@@ -425,7 +425,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: the LoLA hot path here runs on one GPU; --gpus must be 1 "
-              "(per-(sequence, KV head) chains shard with no collectives; see the design notes)", file=sys.stderr)
+              "(the (sequence, KV head) chains are independent, so they would shard over GPUs with no "
+              "collectives)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         copy_calibration()
