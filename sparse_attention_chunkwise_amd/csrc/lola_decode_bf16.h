@@ -15,7 +15,7 @@
 //             hi/lo rows (written when each key entered the cache), the
 //             leaving key's are computed, phi(k) = [softmax(W k); softmax(-W k)]
 //             by MFMA with W in three bf16 parts; n^T = H^T phi^T with H and
-//             phi in bf16 hi/lo parts, d = phi . s; then the pair with the
+//             phi in bf16 hi/lo parts, d = phi . s (s in three bf16 parts); then the pair with the
 //             lowest SRE (newest on a tie) is folded into H, s by one outer
 //             product when the candidates exceed the capacity, and the leaving
 //             key takes its cache slot with its feature row.
@@ -30,7 +30,7 @@ namespace lola {
 constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
 
 struct DecSmem {
-    size_t HhT, HlT, Wl, sP, cposL, esc, phiE, phiF, xrow, stVT, nE, phiFop, misc, total;
+    size_t HhT, HlT, Wl, sP, sParts, cposL, esc, phiE, phiF, xrow, stVT, nE, phiFop, misc, total;
 };
 
 // The two arrays sized by the cache capacity come last: every other offset is a
@@ -45,6 +45,7 @@ __host__ __device__ constexpr DecSmem dec_smem(int C)
     m.HlT = off;   off += align_up(sizeof(uint16_t) * (size_t)D * (F + 8), 16);
     m.Wl = off;    off += align_up(sizeof(uint16_t) * 3 * (size_t)(F / 2) * (D + 8), 16);  // W parts, padded rows
     m.sP = off;    off += align_up(sizeof(float) * F, 16);
+    m.sParts = off; off += align_up(sizeof(uint16_t) * 3 * F, 16);  // s in three bf16 parts, operand order
     m.phiE = off;  off += align_up(sizeof(float) * F, 16);
     m.phiF = off;  off += align_up(sizeof(float) * F, 16);
     m.xrow = off;  off += align_up(sizeof(float) * D, 16);
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     uint16_t* HhT = (uint16_t*)(smem + sm.HhT);
     uint16_t* HlT = (uint16_t*)(smem + sm.HlT);
     float* sP = (float*)(smem + sm.sP);
+    uint16_t* sParts = (uint16_t*)(smem + sm.sParts);
     int* cposL = (int*)(smem + sm.cposL);
     float* esc = (float*)(smem + sm.esc);
     float* phiE = (float*)(smem + sm.phiE);
@@ -213,7 +215,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             *(uint2*)(HhT + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
             *(uint2*)(HlT + o) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
         }
-        for (int i = tid; i < F; i += 256) sP[perm_pos(i)] = ch.s()[i];
+        for (int i = tid; i < F; i += 256) {
+            const float x = ch.s()[i];
+            const int o = perm_pos(i);
+            sP[o] = x;
+            const uint16_t p1 = bf16_bits(x);
+            const float r1 = x - bf16_val(p1);
+            const uint16_t p2 = bf16_bits(r1);
+            sParts[o] = p1;
+            sParts[F + o] = p2;
+            sParts[2 * F + o] = bf16_bits(r1 - bf16_val(p2));
+        }
         for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
     }
     // query frags (columns r16 < G); the leaving key's row (wave 3, column 0) and
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                                      __uint_as_float(vq[p][dt].y << 16), __uint_as_float(vq[p][dt].y & 0xffff0000u)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float df = (acc[p][i] + acc2[p][i]) * inv[p] - (cv[p] ? vv[i] : 0.f);
+                    const float df = (acc[p][i] + acc2[p][i]) * inv[p] - vv[i];
                     es[p] += df * df;
                 }
                 if (nout && nout[p])
@@ -286,21 +298,26 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             e[p] = es[p];
         }
     };
-    // 1 / d with d = s . (phi hi + phi lo): the feature values the MFMAs see (the
-    // prefill scan scores with the same 16-bit features)
+    // d = s . (phi hi + phi lo), the feature values the MFMAs see, by MFMA as in the
+    // prefill scan: A rows 4q, 4q + 1, 4q + 2 hold the three bf16 parts of s (row
+    // 4q + 3 zero), so every lane group receives d of its column (candidate r16) in
+    // its own result rows; the products are exact and the sums fp32
     auto dot_s = [&](const bf16x8* bh, const bf16x8* bl) -> float {
-        float dd = 0.f;
+        const int row = (r16 & 3) < 3 ? (r16 & 3) : 2;
+        const uint32_t keepm = (r16 & 3) < 3 ? 0xffffffffu : 0u;
+        floatx4 dac = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mf = 0; mf < FM; ++mf) {
-            const u16x8 uh = __builtin_bit_cast(u16x8, bh[mf]), ul = __builtin_bit_cast(u16x8, bl[mf]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dd += (bf16_val(uh[j]) + bf16_val(ul[j])) * sP[mf * 32 + qg * 8 + j];
+            uint4 x = *(const uint4*)(sParts + row * F + mf * 32 + qg * 8);
+            x.x &= keepm;
+            x.y &= keepm;
+            x.z &= keepm;
+            x.w &= keepm;
+            const bf16x8 as = __builtin_bit_cast(bf16x8, x);
+            dac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, bh[mf], dac, 0, 0, 0);
+            dac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, bl[mf], dac, 0, 0, 0);
         }
-        return quad_sum(dd);
-    };
-    auto inv_d = [&](const bf16x8* bh, const bf16x8* bl) -> float {
-        const float dd = dot_s(bh, bl);
-        return dd > 0.f ? 1.f / dd : 0.f;
+        return (dac[0] + dac[1]) + dac[2];
     };
     // SRE of P tiles whose features are computed here from the key fragments kb[p]
     auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
@@ -637,9 +654,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             for (int p = 0; p < 2; ++p) {
                 cv[p] = tl[p] * 16 + r16 < cnt;
 #pragma unroll
+                // (slots past the count are scored as stored -- zero or an earlier
+                // pair's finite row -- and their errors are not kept)
                 for (int mf = 0; mf < FM; ++mf) {
-                    bh[p][mf] = __builtin_bit_cast(bf16x8, cv[p] ? fq[p][mf] : make_uint4(0, 0, 0, 0));
-                    bl[p][mf] = __builtin_bit_cast(bf16x8, cv[p] ? fq[p][FM + mf] : make_uint4(0, 0, 0, 0));
+                    bh[p][mf] = __builtin_bit_cast(bf16x8, fq[p][mf]);
+                    bl[p][mf] = __builtin_bit_cast(bf16x8, fq[p][FM + mf]);
                 }
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vv[p][dt] = vq[p][dt];
