@@ -59,19 +59,6 @@ __host__ __device__ constexpr DecSmem dec_smem(int C)
     return m;
 }
 
-// e^x as 2^(x log2 e): the product is carried in two floats (log2 e split into
-// a float and its remainder, as in Cody and Waite's argument reduction), so the
-// hardware 2^ instruction sees an argument good to about 2^-40 relative and
-// 2^r = 1 + r ln 2 covers the small remainder r.  Arguments here are <= 0.
-__device__ __forceinline__ float exp_acc(float x)
-{
-    constexpr float kL1 = 1.44269502162933349609375f;  // log2(e) rounded to float
-    constexpr float kL2 = 1.9259629911783447e-08f;     // log2(e) - kL1
-    const float t = x * kL1;
-    const float r = fmaf(x, kL1, -t) + x * kL2;
-    return __builtin_amdgcn_exp2f(t) * fmaf(r, 0.693147180559945309f, 1.0f);
-}
-
 // phi = [softmax(W k); softmax(-W k)] of P tiles of 16 keys (key r16 of tile p in
 // column r16 of kb[p]): z^T = W K^T by MFMA with W in three bf16 parts (exact
 // products against bf16 keys, fp32 sums; the W operands are read once for all P

@@ -12,9 +12,11 @@
 //     O^T = H_c^T phi(q)^T and Z = s_c . phi(q) start the accumulators
 //     (linear read of the interval-start state, LoLA summary section
 //     "Inferentiestrategie", step 4);
-//   - keys in blocks of 32 (the window span of the interval, then the cache
+//   - keys in blocks of 64 (the window span of the interval, then the cache
 //     snapshot): K, V^T and phi(K) are staged in LDS with 16-byte loads, the
-//     next block prefetched into registers; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
+//     next block prefetched into registers (the first one before phi(q) is
+//     computed), and each block is consumed in two steps of 32 keys so the
+//     per-step registers stay those of a 32-key block; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
 //     for keys that left the window inside the interval, online softmax with
 //     a running max floored at 0 so the linear terms carry e^-M, and
 //     O^T += V^T P^T;
@@ -26,7 +28,8 @@
 namespace lola {
 
 constexpr int kOutRows = 256;  // query rows per workgroup
-constexpr int kKeyBlock = 32;  // (two row tiles per wave with 64-key blocks spill registers)
+constexpr int kKeyBlock = 64;  // keys staged per block: one load round trip per 64 keys
+constexpr int kKeyStep = 32;   // keys per compute step (two row tiles per wave with 64-key steps spill registers)
 constexpr int kOutThreads = 512;  // 8 waves x 32 query rows
 
 struct OutSmem {
@@ -52,7 +55,7 @@ __host__ __device__ constexpr OutSmem out_smem(int C)
     return m;
 }
 
-// position of key k (0..31) of a 32-key half block in the P^T / V^T operand order
+// position of key k (0..31) of a 32-key step in the P^T / V^T operand order
 __device__ __forceinline__ int key_perm(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
 
 template <int D, int F>
@@ -138,6 +141,55 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     }
     __syncthreads();
 
+    // ---- keys: window span [sp0, ep) then the snapshot cache ----
+    const int Cp = d.C > 0 ? d.C : 1;
+    const int64_t sp0 = ap - w > 0 ? ap - w : 0;
+    const int nSpan = (int)(ep - sp0);
+    const int ccnt = ((const int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c];
+    const int* sref = srefL;
+    const int nK = nSpan + ccnt;
+    const int xs0 = (int)(sp0 - (t0 - w));
+    const float tau = d.tau;
+    const int64_t lastPend = ep - 1 - w;
+    constexpr int KU = (KB * D / 8 + NT - 1) / NT;  // 16-byte units per thread for K
+    constexpr int PU = (KB * F / 8 + NT - 1) / NT;  // for phi(K)
+    constexpr int VPU = (KB / 2) * (D / 8);         // (key pair, 8-value unit) items for V
+    static_assert(VPU <= NT, "one V key-pair unit per thread at most");
+    uint4 pk[KU], pv[2], pp[PU];
+    // Row addresses of the KB keys of block j go to table j % 2, written by one
+    // wave two blocks ahead of the prefetch that reads them.
+    auto fill_rows = [&](int j, int i) {
+        const int kidx = j * KB + i, kc = kidx < nK ? kidx : 0;
+        const int ref = kc < nSpan ? xs0 + kc : sref[kc - nSpan];
+        rowK[(j & 1) * KB + i] = ref_k<bf16>(a, chain, b, g, ref);
+        rowV[(j & 1) * KB + i] = ref_v<bf16>(a, chain, b, g, ref);
+    };
+#define LOLA_OUT_PREFETCH(BASE)                                                                                      \
+    do {                                                                                                             \
+        const int tb = (((BASE) / KB) & 1) * KB;                                                                     \
+        _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
+            const int idx = tid + k * NT, kr = (idx / (D / 8)) % KB, un = idx % (D / 8);                             \
+            const uint4 k4 = *(const uint4*)(rowK[tb + kr] + un * 8);                                                \
+            pk[k] = (BASE) + kr < nK ? k4 : make_uint4(0, 0, 0, 0);                                                  \
+        }                                                                                                            \
+        if (tid < VPU) {                                                                                             \
+            const int pr = tid % (KB / 2), un = tid / (KB / 2);                                                      \
+            _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
+                const uint4 v4 = *(const uint4*)(rowV[tb + 2 * pr + k] + un * 8);                                   \
+                pv[k] = (BASE) + 2 * pr + k < nK ? v4 : make_uint4(0, 0, 0, 0);                                      \
+            }                                                                                                        \
+        }                                                                                                            \
+        _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
+            const int idx = tid + k * NT, kr = (idx / (F / 8)) % KB, un = idx % (F / 8), kidx = (BASE) + kr;         \
+            const bool want = kidx < nSpan && sp0 + kidx <= lastPend;                                                \
+            const uint4 p4 = *(const uint4*)(ws_phiS(a, chain, xs0 + (want ? kidx : 0)) + un * 8);                   \
+            pp[k] = want ? p4 : make_uint4(0, 0, 0, 0);                                                              \
+        }                                                                                                            \
+    } while (0)
+    if (tid < 2 * KB) fill_rows(tid / KB, tid % KB);
+    __syncthreads();  // tables of blocks 0 and 1
+    if (nK > 0) LOLA_OUT_PREFETCH(0);  // in flight while phi(q) and the linear read run
+
     // ---- phi(q): z^T = W Q^T (W hi + lo), two softmax halves per query ----
     bf16x8 pf[RT][FM];
     float zl[RT];
@@ -216,56 +268,8 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) { Zp[rt] = qg == 0 ? zl[rt] : 0.f; mrun[rt] = 0.f; }
 
-    // ---- keys: window span [sp0, ep) then the snapshot cache ----
-    const int Cp = d.C > 0 ? d.C : 1;
-    const int64_t sp0 = ap - w > 0 ? ap - w : 0;
-    const int nSpan = (int)(ep - sp0);
-    const int ccnt = ((const int*)(a.ws + a.wl.snapN))[(size_t)chain * NI + c];
-    const int* sref = srefL;
-    const int nK = nSpan + ccnt;
-    const int xs0 = (int)(sp0 - (t0 - w));
-    const float tau = d.tau;
-    const int64_t lastPend = ep - 1 - w;
-    constexpr int KU = (KB * D / 8 + NT - 1) / NT;  // 16-byte units per thread for K
-    constexpr int PU = (KB * F / 8 + NT - 1) / NT;  // for phi(K)
-    constexpr int VPU = (KB / 2) * (D / 8);         // (key pair, 8-value unit) items for V
-    static_assert(VPU <= NT, "one V key-pair unit per thread at most");
-    uint4 pk[KU], pv[2], pp[PU];
-    // Row addresses of the KB keys of block j go to table j % 2, written by one
-    // wave two blocks ahead of the prefetch that reads them.
-    auto fill_rows = [&](int j, int i) {
-        const int kidx = j * KB + i, kc = kidx < nK ? kidx : 0;
-        const int ref = kc < nSpan ? xs0 + kc : sref[kc - nSpan];
-        rowK[(j & 1) * KB + i] = ref_k<bf16>(a, chain, b, g, ref);
-        rowV[(j & 1) * KB + i] = ref_v<bf16>(a, chain, b, g, ref);
-    };
-#define LOLA_OUT_PREFETCH(BASE)                                                                                      \
-    do {                                                                                                             \
-        const int tb = (((BASE) / KB) & 1) * KB;                                                                     \
-        _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
-            const int idx = tid + k * NT, kr = (idx / (D / 8)) % KB, un = idx % (D / 8);                             \
-            const uint4 k4 = *(const uint4*)(rowK[tb + kr] + un * 8);                                                \
-            pk[k] = (BASE) + kr < nK ? k4 : make_uint4(0, 0, 0, 0);                                                  \
-        }                                                                                                            \
-        if (tid < VPU) {                                                                                             \
-            const int pr = tid % (KB / 2), un = tid / (KB / 2);                                                      \
-            _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                                          \
-                const uint4 v4 = *(const uint4*)(rowV[tb + 2 * pr + k] + un * 8);                                   \
-                pv[k] = (BASE) + 2 * pr + k < nK ? v4 : make_uint4(0, 0, 0, 0);                                      \
-            }                                                                                                        \
-        }                                                                                                            \
-        _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
-            const int idx = tid + k * NT, kr = (idx / (F / 8)) % KB, un = idx % (F / 8), kidx = (BASE) + kr;         \
-            const bool want = kidx < nSpan && sp0 + kidx <= lastPend;                                                \
-            const uint4 p4 = *(const uint4*)(ws_phiS(a, chain, xs0 + (want ? kidx : 0)) + un * 8);                   \
-            pp[k] = want ? p4 : make_uint4(0, 0, 0, 0);                                                              \
-        }                                                                                                            \
-    } while (0)
-    if (tid < 2 * KB) fill_rows(tid / KB, tid % KB);
-    __syncthreads();  // tables of blocks 0 and 1
-    if (nK > 0) LOLA_OUT_PREFETCH(0);
     for (int base = 0; base < nK; base += KB) {
-        __syncthreads();  // the previous block (or W) and the table of block base / KB are no longer read
+        __syncthreads();  // the previous block and the table of block base / KB are no longer read
         if (tid < KB && base + 2 * KB < nK) fill_rows(base / KB + 2, tid);
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
@@ -292,84 +296,84 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         }
         __syncthreads();
         if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB);
-        const bool anyPend = base < nSpan && sp0 + base <= lastPend;
-
-        constexpr int KT = KB / 16;  // key tiles per block
-        floatx4 sT[RT][KT], kT[RT][KT];
 #pragma unroll
-        for (int tt = 0; tt < KT; ++tt) {
+        for (int st = 0; st < KB / kKeyStep; ++st) {
+            const int sb = base + st * kKeyStep;  // first key of this step
+            if (sb >= nK) break;                  // (uniform)
+            const bool anyPend = sb < nSpan && sp0 + sb <= lastPend;
+            constexpr int KT = kKeyStep / 16;  // key tiles per step
+            floatx4 sT[RT][KT], kT[RT][KT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = kT[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < KT; ++tt) {
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                const bf16x8 ka = *(const bf16x8*)(Ks + (tt * 16 + r16) * KP + ks * 32 + qg * 8);
+                for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = kT[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                const int kr = st * kKeyStep + tt * 16 + r16;  // staged row of this lane's key
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rt][ks], sT[rt][tt], 0, 0, 0);
-            }
-            if (anyPend) {
+                for (int ks = 0; ks < DS; ++ks) {
+                    const bf16x8 ka = *(const bf16x8*)(Ks + kr * KP + ks * 32 + qg * 8);
 #pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    const bf16x8 pa = *(const bf16x8*)(Pk + (tt * 16 + r16) * PP + mf * 32 + qg * 8);
+                    for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rt][ks], sT[rt][tt], 0, 0, 0);
+                }
+                if (anyPend) {
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) kT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, pf[rt][mf], kT[rt][tt], 0, 0, 0);
+                    for (int mf = 0; mf < FM; ++mf) {
+                        const bf16x8 pa = *(const bf16x8*)(Pk + kr * PP + mf * 32 + qg * 8);
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) kT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, pf[rt][mf], kT[rt][tt], 0, 0, 0);
+                    }
                 }
             }
-        }
-        bf16x8 pb[RT][KB / 32];
+            bf16x8 pb[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            // the lane's KB/4 keys: base + tt*16 + qg*4 + i (tt = j / 4, i = j % 4); key j
-            // sits in slot j % 8 of the P^T operand of half j / 8
-            constexpr int NJ = KB / 4;
-            float lg[NJ];
-            int kind[NJ];
-            float bmax = -INFINITY;
-            // query position relative to the span start; span key kidx sits at sp0 + kidx
-            const int tr = qv[rt] ? (int)(tq[rt] - sp0) : -1;
+            for (int rt = 0; rt < RT; ++rt) {
+                // the lane's 8 keys: sb + tt*16 + qg*4 + i (tt = j / 4, i = j % 4); key j
+                // sits in slot j of the P^T operand
+                constexpr int NJ = kKeyStep / 4;
+                float lg[NJ];
+                int kind[NJ];
+                float bmax = -INFINITY;
+                // query position relative to the span start; span key kidx sits at sp0 + kidx
+                const int tr = qv[rt] ? (int)(tq[rt] - sp0) : -1;
+                // kind 1: softmax key (in the query's window, or a cache key), 2: linear key
+                // (left the window inside the interval, before the query), 0: masked; all
+                // selects, no branches
 #pragma unroll
-            // kind 1: softmax key (in the query's window, or a cache key), 2: linear key
-            // (left the window inside the interval, before the query), 0: masked; all
-            // selects, no branches
-            for (int j = 0; j < NJ; ++j) {
-                const int tt = j >> 2, i = j & 3;
-                const int kidx = base + tt * 16 + qg * 4 + i;
-                const int kspan = kidx <= tr ? (kidx >= tr - w + 1 ? 1 : 2) : 0;
-                kind[j] = (tr >= 0 && kidx < nK) ? (kidx < nSpan ? kspan : 1) : 0;
-                lg[j] = tau * sT[rt][tt][i];
-                bmax = fmaxf(bmax, kind[j] == 1 ? lg[j] : -INFINITY);
-            }
-            bmax = quad_max(bmax);
-            const float mnew = fmaxf(mrun[rt], bmax);
-            const float resc = __expf(mrun[rt] - mnew);
-            mrun[rt] = mnew;
+                for (int j = 0; j < NJ; ++j) {
+                    const int tt = j >> 2, i = j & 3;
+                    const int kidx = sb + tt * 16 + qg * 4 + i;
+                    const int kspan = kidx <= tr ? (kidx >= tr - w + 1 ? 1 : 2) : 0;
+                    kind[j] = (tr >= 0 && kidx < nK) ? (kidx < nSpan ? kspan : 1) : 0;
+                    lg[j] = tau * sT[rt][tt][i];
+                    bmax = fmaxf(bmax, kind[j] == 1 ? lg[j] : -INFINITY);
+                }
+                bmax = quad_max(bmax);
+                const float mnew = fmaxf(mrun[rt], bmax);
+                const float resc = __expf(mrun[rt] - mnew);
+                mrun[rt] = mnew;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
-            Zp[rt] *= resc;
-            const float elin = __expf(-mnew);
-#pragma unroll
-            for (int hh = 0; hh < KB / 32; ++hh) {
+                for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
+                Zp[rt] *= resc;
+                const float elin = __expf(-mnew);
                 u16x8 u;
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int j = hh * 8 + jj, tt = j >> 2, i = j & 3;
+                for (int j = 0; j < NJ; ++j) {
+                    const int tt = j >> 2, i = j & 3;
                     const float e1 = __expf(lg[j] - mnew), e2 = kT[rt][tt][i] * elin;
                     const float pv_ = kind[j] == 1 ? e1 : (kind[j] == 2 ? e2 : 0.f);
                     Zp[rt] += pv_;
-                    u[jj] = bf16_bits(pv_);
+                    u[j] = bf16_bits(pv_);
                 }
-                pb[rt][hh] = __builtin_bit_cast(bf16x8, u);
+                pb[rt] = __builtin_bit_cast(bf16x8, u);
             }
-        }
-        // O^T += V^T P^T
+            // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int hh = 0; hh < KB / 32; ++hh) {
-                const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + hh * 32 + qg * 8);
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + st * kKeyStep + qg * 8);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt][hh], O[rt][dt], 0, 0, 0);
+                    O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], O[rt][dt], 0, 0, 0);
             }
+        }
     }
 
 #undef LOLA_OUT_PREFETCH

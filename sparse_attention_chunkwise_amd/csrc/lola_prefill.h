@@ -219,6 +219,23 @@ __global__ __launch_bounds__(256) void prologue_kernel(Args a)
     }
 }
 
+// bf16 bits of x, rounded to nearest even (finite x), and the float a bf16 holds
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// e^x as 2^(x log2 e): the product is carried in two floats (log2 e split into
+// a float and its remainder, as in Cody and Waite's argument reduction), so the
+// hardware 2^ instruction sees an argument good to about 2^-40 relative and
+// 2^r = 1 + r ln 2 covers the small remainder r.  Arguments here are <= 0.
+__device__ __forceinline__ float exp_acc(float x)
+{
+    constexpr float kL1 = 1.44269502162933349609375f;  // log2(e) rounded to float
+    constexpr float kL2 = 1.9259629911783447e-08f;     // log2(e) - kL1
+    const float t = x * kL1;
+    const float r = fmaf(x, kL1, -t) + x * kL2;
+    return __builtin_amdgcn_exp2f(t) * fmaf(r, 0.693147180559945309f, 1.0f);
+}
+
 // Prologue for bf16 io: same rows and layouts, computed 16 rows per wave with
 // MFMA.  z^T = W x^T uses W in three bf16 parts (the products with the bf16 key
 // are exact, sums in fp32); lane (r16, qg) then holds features ft*16 + 4qg + i of
@@ -324,8 +341,8 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
     for (int ft = 0; ft < FTH; ++ft)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ep[ft][i] = expf(zt[ft][i] - zmax);
-            en[ft][i] = expf(zmin - zt[ft][i]);
+            ep[ft][i] = exp_acc(zt[ft][i] - zmax);
+            en[ft][i] = exp_acc(zmin - zt[ft][i]);
             sp += ep[ft][i];
             sn += en[ft][i];
         }
@@ -333,13 +350,14 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
     sn = quad_sum(sn);
     if (row >= X + C) return;
     const bool valid = src != nullptr;
+    const float isp = valid ? 1.f / sp : 0.f, isn = valid ? 1.f / sn : 0.f;
     float ph[2 * FTH][4];  // feature tile T: + half T < FTH, - half T >= FTH
 #pragma unroll
     for (int ft = 0; ft < FTH; ++ft)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ph[ft][i] = valid ? ep[ft][i] / sp : 0.f;
-            ph[FTH + ft][i] = valid ? en[ft][i] / sn : 0.f;
+            ph[ft][i] = ep[ft][i] * isp;
+            ph[FTH + ft][i] = en[ft][i] * isn;
         }
     uint16_t* ps = row < X ? ws_phiS(a, chain, row) : ws_cphiS(a, chain, row - X);
     if (fp32_rows) {  // fp32 rows: only the one-workgroup scan reads them
@@ -355,8 +373,8 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = ph[2 * m + (j >> 2)][j & 3];
-            hi[j] = from_f32<bf16>(x).x;
-            lo[j] = from_f32<bf16>(x - __uint_as_float((uint32_t)hi[j] << 16)).x;
+            hi[j] = bf16_bits(x);
+            lo[j] = bf16_bits(x - bf16_val(hi[j]));
         }
         *(u16x8*)(ps + m * 32 + qg * 8) = hi;
         *(u16x8*)(ps + F + m * 32 + qg * 8) = lo;
@@ -427,8 +445,6 @@ __host__ __device__ inline ScanSmem scan_smem(int D, int F, int C, int L, int es
     return m;
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-__device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 __device__ __forceinline__ void load4(const float* p, float* o)
 {
