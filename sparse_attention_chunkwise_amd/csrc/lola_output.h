@@ -19,7 +19,10 @@
 //     per-step registers stay those of a 32-key block; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
 //     for keys that left the window inside the interval, online softmax with
 //     a running max floored at 0 so the linear terms carry e^-M, and
-//     O^T += V^T P^T;
+//     O^T += V^T P^T; the blocks past the window span (cache keys only) skip
+//     phi(K), kappa and the key classification, and move the softmax
+//     reference only when a logit exceeds it by more than 8, so O and Z are
+//     rarely rescaled there;
 //   - o = O / Z with one shared denominator.
 #pragma once
 
@@ -30,6 +33,7 @@ namespace lola {
 constexpr int kOutRows = 256;  // query rows per workgroup
 constexpr int kKeyBlock = 64;  // keys staged per block: one load round trip per 64 keys
 constexpr int kKeyStep = 32;   // keys per compute step (two row tiles per wave with 64-key steps spill registers)
+constexpr float kRescaleGap = 8.f;  // cache blocks: the softmax reference moves when a logit exceeds it by more
 constexpr int kOutThreads = 512;  // 8 waves x 32 query rows
 
 struct OutSmem {
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
         rowK[(j & 1) * KB + i] = ref_k<bf16>(a, chain, b, g, ref);
         rowV[(j & 1) * KB + i] = ref_v<bf16>(a, chain, b, g, ref);
     };
-#define LOLA_OUT_PREFETCH(BASE)                                                                                      \
+#define LOLA_OUT_PREFETCH(BASE, PHI)                                                                                 \
     do {                                                                                                             \
         const int tb = (((BASE) / KB) & 1) * KB;                                                                     \
         _Pragma("unroll") for (int k = 0; k < KU; ++k) {                                                             \
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                 pv[k] = (BASE) + 2 * pr + k < nK ? v4 : make_uint4(0, 0, 0, 0);                                      \
             }                                                                                                        \
         }                                                                                                            \
-        _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                             \
+        if (PHI) _Pragma("unroll") for (int k = 0; k < PU; ++k) {                                                    \
             const int idx = tid + k * NT, kr = (idx / (F / 8)) % KB, un = idx % (F / 8), kidx = (BASE) + kr;         \
             const bool want = kidx < nSpan && sp0 + kidx <= lastPend;                                                \
             const uint4 p4 = *(const uint4*)(ws_phiS(a, chain, xs0 + (want ? kidx : 0)) + un * 8);                   \
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
     } while (0)
     if (tid < 2 * KB) fill_rows(tid / KB, tid % KB);
     __syncthreads();  // tables of blocks 0 and 1
-    if (nK > 0) LOLA_OUT_PREFETCH(0);  // in flight while phi(q) and the linear read run
+    if (nK > 0) LOLA_OUT_PREFETCH(0, true);  // in flight while phi(q) and the linear read run
 
     // ---- phi(q): z^T = W Q^T (W hi + lo), two softmax halves per query ----
     bf16x8 pf[RT][FM];
@@ -268,7 +272,9 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) { Zp[rt] = qg == 0 ? zl[rt] : 0.f; mrun[rt] = 0.f; }
 
-    for (int base = 0; base < nK; base += KB) {
+    // blocks that hold window-span keys (window, linear and masked keys)
+    int base = 0;
+    for (; base < nK && base < nSpan; base += KB) {
         __syncthreads();  // the previous block and the table of block base / KB are no longer read
         if (tid < KB && base + 2 * KB < nK) fill_rows(base / KB + 2, tid);
 #pragma unroll
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
             if (idx < KB * F / 8) *(uint4*)(Pk + kr * PP + un * 8) = pp[k];
         }
         __syncthreads();
-        if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB);
+        if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB, true);
 #pragma unroll
         for (int st = 0; st < KB / kKeyStep; ++st) {
             const int sb = base + st * kKeyStep;  // first key of this step
@@ -362,6 +368,92 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                     const float pv_ = kind[j] == 1 ? e1 : (kind[j] == 2 ? e2 : 0.f);
                     Zp[rt] += pv_;
                     u[j] = bf16_bits(pv_);
+                }
+                pb[rt] = __builtin_bit_cast(bf16x8, u);
+            }
+            // O^T += V^T P^T
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 va = *(const bf16x8*)(VT + (dt * 16 + r16) * VP + st * kKeyStep + qg * 8);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    O[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], O[rt][dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // Blocks past the window span hold cache keys only (and, in the last block, slots
+    // past the count, masked): no linear keys, so no phi(K) rows, no kappa and no
+    // classification.  The softmax reference m of a row moves only when a logit exceeds
+    // it by more than kRescaleGap (decided for the whole wave), so O and Z are rarely
+    // rescaled; weights e^(logit - m) stay below e^kRescaleGap, and any m gives the same
+    // o = O / Z.
+    for (; base < nK; base += KB) {
+        __syncthreads();  // the previous block and the table of block base / KB are no longer read
+        if (tid < KB && base + 2 * KB < nK) fill_rows(base / KB + 2, tid);
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int idx = tid + k * NT, kr = idx / (D / 8), un = idx % (D / 8);
+            if (idx < KB * D / 8) *(uint4*)(Ks + kr * KP + un * 8) = pk[k];
+        }
+        if (tid < VPU) {
+            const int pr = tid % (KB / 2), un = tid / (KB / 2), kc = (2 * pr / 32) * 32 + key_perm((2 * pr) % 32);
+            const uint32_t w0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w}, w1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                const uint32_t hi = (w1[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                *(uint32_t*)(VT + (un * 8 + j) * VP + kc) = lo | (hi << 16);
+            }
+        }
+        __syncthreads();
+        if (base + KB < nK) LOLA_OUT_PREFETCH(base + KB, false);
+#pragma unroll
+        for (int st = 0; st < KB / kKeyStep; ++st) {
+            const int sb = base + st * kKeyStep;  // first key of this step
+            if (sb >= nK) break;                  // (uniform)
+            constexpr int KT = kKeyStep / 16;
+            floatx4 sT[RT][KT];
+#pragma unroll
+            for (int tt = 0; tt < KT; ++tt) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                const int kr = st * kKeyStep + tt * 16 + r16;
+#pragma unroll
+                for (int ks = 0; ks < DS; ++ks) {
+                    const bf16x8 ka = *(const bf16x8*)(Ks + kr * KP + ks * 32 + qg * 8);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) sT[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rt][ks], sT[rt][tt], 0, 0, 0);
+                }
+            }
+            bf16x8 pb[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                // the lane's 8 keys: sb + tt*16 + qg*4 + i (tt = j / 4, i = j % 4), slot j of P^T
+                constexpr int NJ = kKeyStep / 4;
+                float lg[NJ];
+                float bmax = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int kidx = sb + (j >> 2) * 16 + qg * 4 + (j & 3);
+                    lg[j] = kidx < nK ? tau * sT[rt][j >> 2][j & 3] : -INFINITY;
+                    bmax = fmaxf(bmax, lg[j]);
+                }
+                bmax = quad_max(bmax);
+                if (__builtin_amdgcn_ballot_w64(bmax > mrun[rt] + kRescaleGap) != 0ull) {
+                    const float mnew = fmaxf(mrun[rt], bmax);
+                    const float resc = __expf(mrun[rt] - mnew);
+                    mrun[rt] = mnew;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
+                    Zp[rt] *= resc;
+                }
+                u16x8 u;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float e1 = __expf(lg[j] - mrun[rt]);  // 0 for a masked slot
+                    Zp[rt] += e1;
+                    u[j] = bf16_bits(e1);
                 }
                 pb[rt] = __builtin_bit_cast(bf16x8, u);
             }
