@@ -271,9 +271,11 @@ struct Args {
 // writes the header; only the split scan does, and it broadcasts its test.)
 __device__ __forceinline__ bool state_ok(const Args& a, bool allow_faulted = false)
 {
-    const StateHeader* h = (const StateHeader*)a.state;
-    return h->magic == kMagic && h->version == kVersion && h->cfg_hash == a.hash && h->batch == a.B &&
-           (allow_faulted || h->fault == 0);
+    // the 32 header bytes in one load, and no early exit between the tests: the
+    // fields are requested together instead of one round trip after another
+    const StateHeader h = *(const StateHeader*)a.state;
+    return (h.magic == kMagic) & (h.version == kVersion) & (h.cfg_hash == a.hash) & (h.batch == a.B) &
+           (allow_faulted | (h.fault == 0));
 }
 
 // Tokens sequence b consumes in this call: its entry of the per-sequence counts
