@@ -17,12 +17,11 @@
 //     next block prefetched into registers (the first one before phi(q) is
 //     computed), and each block is consumed in two steps of 32 keys so the
 //     per-step registers stay those of a 32-key block; S^T = K Q^T, kappa^T = phi(K) phi(q)^T
-//     for keys that left the window inside the interval, online softmax with
-//     a running max floored at 0 so the linear terms carry e^-M, and
-//     O^T += V^T P^T; the blocks past the window span (cache keys only) skip
-//     phi(K), kappa and the key classification, and move the softmax
-//     reference only when a logit exceeds it by more than 8, so O and Z are
-//     rarely rescaled there;
+//     for keys that left the window inside the interval, online softmax
+//     against a reference M >= 0 (the linear terms carry e^-M) that moves only
+//     when a logit exceeds it by more than 8, so O and Z are rarely rescaled,
+//     and O^T += V^T P^T; the blocks past the window span (cache keys only)
+//     skip phi(K), kappa and the key classification;
 //   - o = O / Z with one shared denominator.
 #pragma once
 
@@ -33,7 +32,7 @@ namespace lola {
 constexpr int kOutRows = 256;  // query rows per workgroup
 constexpr int kKeyBlock = 64;  // keys staged per block: one load round trip per 64 keys
 constexpr int kKeyStep = 32;   // keys per compute step (two row tiles per wave with 64-key steps spill registers)
-constexpr float kRescaleGap = 8.f;  // cache blocks: the softmax reference moves when a logit exceeds it by more
+constexpr float kRescaleGap = 8.f;  // the softmax reference moves when a logit exceeds it by more
 constexpr int kOutThreads = 512;  // 8 waves x 32 query rows
 
 struct OutSmem {
@@ -353,12 +352,17 @@ __global__ __launch_bounds__(kOutThreads) void output_kernel_bf16(Args a)
                     bmax = fmaxf(bmax, kind[j] == 1 ? lg[j] : -INFINITY);
                 }
                 bmax = quad_max(bmax);
-                const float mnew = fmaxf(mrun[rt], bmax);
-                const float resc = __expf(mrun[rt] - mnew);
-                mrun[rt] = mnew;
+                // the reference moves only when a logit exceeds it by more than kRescaleGap
+                // (for the whole wave); weights stay below e^kRescaleGap, o = O / Z is unchanged
+                if (__builtin_amdgcn_ballot_w64(bmax > mrun[rt] + kRescaleGap) != 0ull) {
+                    const float mnew = fmaxf(mrun[rt], bmax);
+                    const float resc = __expf(mrun[rt] - mnew);
+                    mrun[rt] = mnew;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
-                Zp[rt] *= resc;
+                    for (int dt = 0; dt < DT; ++dt) O[rt][dt] *= resc;
+                    Zp[rt] *= resc;
+                }
+                const float mnew = mrun[rt];
                 const float elin = __expf(-mnew);
                 u16x8 u;
 #pragma unroll
