@@ -124,6 +124,11 @@ EDGE = [
     ("bf16_max_interval", I.LayerConfig(2, 1, 64, 32, 16, 40, 256, "bf16"), 1, 600),
     ("bf16_max_window", I.LayerConfig(2, 1, 64, 32, 8192, 16, 64, "bf16"), 1, 8300),
     ("bf16_group16", I.LayerConfig(16, 1, 64, 32, 7, 9, 11, "bf16"), 1, 50),
+    # logits with a spread of tens (scale 2 instead of 1/sqrt(128)): the output pass's
+    # softmax reference must move across key blocks, in the window-span blocks and in
+    # the cache blocks (64-key blocks: one straddling span and cache, one full cache
+    # block, one partial)
+    ("bf16_sharp_softmax", I.LayerConfig(8, 2, 128, 64, 16, 96, 32, "bf16", softmax_scale=2.0), 1, 300),
 ]
 
 
@@ -133,7 +138,8 @@ def test_edge_stepped(name, layer, B, T):
     _stepped(layer, B, W, Q, K, V, state_every=4, label=name)
 
 
-ONE_BLOCK = [e for e in EDGE if e[0] in ("bf16_ragged", "bf16_d64", "bf16_max_interval", "bf16_no_cache")]
+ONE_BLOCK = [e for e in EDGE if e[0] in ("bf16_ragged", "bf16_d64", "bf16_max_interval", "bf16_no_cache",
+                                          "bf16_sharp_softmax")]
 
 
 @pytest.mark.parametrize("name,layer,B,T", ONE_BLOCK, ids=[e[0] for e in ONE_BLOCK])
