@@ -218,11 +218,11 @@ lola_status launch_decode(Args& a, hipStream_t s)
         const size_t lds = dec_smem<D, F>(a.d.C).total;
         if (a.d.inc) {
             if (allow_lds(decode_kernel_bf16<D, F, true>, lds) != hipSuccess) return LOLA_ERR_HIP;
-            hipLaunchKernelGGL((decode_kernel_bf16<D, F, true>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+            hipLaunchKernelGGL((decode_kernel_bf16<D, F, true>), dim3(a.B * a.d.Hkv), dim3(kDecThreads), lds, s, a);
             return hip_status(hipGetLastError());
         }
         if (allow_lds(decode_kernel_bf16<D, F, false>, lds) != hipSuccess) return LOLA_ERR_HIP;
-        hipLaunchKernelGGL((decode_kernel_bf16<D, F, false>), dim3(a.B * a.d.Hkv), dim3(256), lds, s, a);
+        hipLaunchKernelGGL((decode_kernel_bf16<D, F, false>), dim3(a.B * a.d.Hkv), dim3(kDecThreads), lds, s, a);
     } else {
         const size_t lds = decode_smem(D, F, a.d.G, a.d.C).total;
         if (allow_lds(decode_kernel<D, F, T>, lds) != hipSuccess) return LOLA_ERR_HIP;

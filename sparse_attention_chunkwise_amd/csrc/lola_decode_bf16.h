@@ -119,12 +119,21 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
 // feature index of operand slot h (see phi_tile) for lane group qg
 __device__ __forceinline__ int slot_feature(int h, int qg) { return (2 * (h >> 3) + ((h & 7) >> 2)) * 16 + qg * 4 + (h & 3); }
 
+// Waves 0..3 run the read, waves 4..7 the management: both read only the step-start
+// state, so the softmax stream over window and cache and the SRE pass over the cache
+// run side by side on the same CU instead of one after the other.
+constexpr int kDecThreads = 512;
+
 template <int D, int F, bool INC>
-__global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
+__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
 {
-    constexpr int NW = 4, Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
-    constexpr int KBL = kDecBlock, KW = KBL / NW;  // keys per block, per wave
-    constexpr int HP = F + 8, VP = KBL + 8;
+    constexpr int NT = kDecThreads, NA = 4, NB = NT / 64 - NA;  // read waves, management waves
+    constexpr int LASTW = NT / 64 - 1;                           // the leaving key's wave
+    constexpr int Fh = F / 2, FM = F / 32, DS = D / 32, DT = D / 16;
+    constexpr int KW = 32;  // keys per step of a read wave
+    constexpr int HP = F + 8, VP = kDecBlock + 8;
+    static_assert(NA * KW == kDecBlock, "the V^T staging area has one 32-key column block per read wave");
+    static_assert(D * F / 4 % NT == 0, "H loads cover the state exactly");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     if (!state_ok(a)) return;  // header mismatch or faulted state: nothing is read or written
     const Dims& d = a.d;
@@ -148,6 +157,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
+    const bool rd = wave < NA;  // a read wave
     Chain ch = chain_of(a, chain);
     const int64_t t = ch.tok();
     const int cnt = min(max(ch.cnt(), 0), C);
@@ -162,35 +172,105 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
     const bf16* kE = w == 0 ? knew : ch.ring_k<bf16>() + (size_t)rs * D;
     const bf16* vE = w == 0 ? vnew : ch.ring_v<bf16>() + (size_t)rs * D;
     const uint16_t* Wb = (const uint16_t*)(a.state + a.sl.Wb) + (size_t)(3 * g) * Fh * D;
+    const int nU = cnt + (hasE ? 1 : 0);
+    const bool foldStep = hasE && nU > C;
 
-    // ---- state in: H^T hi/lo in operand order, s, cache positions ----
+    // ---- keys of the read: window [ws0, t] then cache slots, in groups of 32 ----
+    const int64_t ws0 = t - w + 1 > 0 ? t - w + 1 : 0;
+    const int nWin = w > 0 ? (int)(t - ws0 + 1) : 0;
+    const int nK = nWin + cnt;
+    // row of key kidx (0 <= kidx < nK): window position ws0 + kidx (ring slot
+    // (ws0 + kidx) mod w, the newest being this step's token), then cache slot
+    // kidx - nWin; chosen by selects so that a group's loads issue together
+    const int rs0 = w > 0 ? (int)(ws0 % w) : 0;
+    auto key_row = [&](int kidx, bool v) -> const bf16* {
+        int slot = rs0 + kidx;
+        slot = slot >= w ? slot - w : slot;
+        const bf16* pw = (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)slot * D;
+        const bf16* pc = (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (ptrdiff_t)(kidx - nWin) * D;
+        const bf16* pn = v ? vnew : knew;
+        return kidx < nWin ? (kidx == nWin - 1 ? pn : pw) : pc;
+    };
+    const int ng = (nK + KW - 1) / KW;
+    // groups are dealt to the read waves in turn, wave 0 (which first computes phi(q)
+    // and the linear read) taking the last group of each round
+    const int g0 = (wave + NA - 1) % NA;
+    // A read wave loads its group's key fragments (keys 32 g + tt * 16 + r16, 16 bytes
+    // per lane straight from the key row) and value rows (lane: key pair lane % 16,
+    // 8-value units lane / 16 + 4 j); rows past nK load the last key and are zeroed.
+    constexpr int VNW = (KW / 2) * (D / 8) / 64;
+    static_assert((KW / 2) * (D / 8) % 64 == 0, "value units cover a group exactly");
+    uint4 kq[2][DS], vqa[VNW], vqb[VNW];
+    auto issue = [&](int gg) {
+        const int base = gg * KW;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int kidx = base + tt * 16 + r16;
+            const bf16* kr = key_row(kidx < nK ? kidx : nK - 1, false);
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) kq[tt][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < VNW; ++j) {
+            const int k0 = base + 2 * r16, un = qg + 4 * j;
+            vqa[j] = *(const uint4*)(key_row(k0 < nK ? k0 : nK - 1, true) + un * 8);
+            vqb[j] = *(const uint4*)(key_row(k0 + 1 < nK ? k0 + 1 : nK - 1, true) + un * 8);
+        }
+    };
+
+    // ---- SRE pass over the cache (management waves): to choose a victim, or
+    //      (incremental decode) to compute the stored n, d of every cached pair afresh ----
+    const bool scoreCache = INC ? (!incValid && cnt > 0) : foldStep;
+    const bool storedScores = INC && incValid && foldStep;
+    const int nT = (cnt + 15) / 16;
+    const int bw = wave - NA;
+    // features of the cached keys come from the state (hi | lo rows in operand order)
+    uint4 fq[2 * FM];
+    uint2 vq[DT];
+    auto tile_load = [&](int tt) {
+        const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
+        const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
+        const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
+#pragma unroll
+        for (int mf = 0; mf < FM; ++mf) {
+            fq[mf] = *(const uint4*)(pr + mf * 32);
+            fq[FM + mf] = *(const uint4*)(pr + F + mf * 32);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vq[dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
+    };
+
+    // ---- state in: H^T hi/lo in operand order, W parts, s, cache positions ----
     {
         const float* Hst = ch.H();  // [D][F]
-        constexpr int HN = D * F / 4 / 256;  // float4 per thread, all loaded before any is used
-        constexpr int WN = 3 * Fh * D / 8 / 256;  // 16-byte pieces of the W parts per thread
-        // W parts to LDS in batches of WB pieces (all loads of a batch issued before
-        // any is stored; larger batches would need more registers than the wave has)
-        constexpr int WB = WN % 4 == 0 ? 4 : (WN % 3 == 0 ? 3 : 1);
-        // H (from HBM, the longest wait) is requested first, all of it; the W batches
-        // (L2 hits) are stored to LDS while it is in flight
+        constexpr int HN = D * F / 4 / NT;  // float4 per thread, all loaded before any is used
+        constexpr int WTOT = 3 * Fh * D / 8, WN = (WTOT + NT - 1) / NT;  // 16-byte pieces of the W parts
+        // W parts to LDS in batches of WB pieces (all loads of a batch issued before any
+        // is stored); H (from HBM, the longest wait) is requested first, all of it, and
+        // the W batches (L2 hits) are stored to LDS while it is in flight
+        constexpr int WB = WN % 3 == 0 ? 3 : (WN % 2 == 0 ? 2 : 1);
         float4 hv4[HN];
 #pragma unroll
-        for (int k = 0; k < HN; ++k) hv4[k] = *(const float4*)(Hst + (size_t)(tid + k * 256) * 4);
+        for (int k = 0; k < HN; ++k) hv4[k] = *(const float4*)(Hst + (size_t)(tid + k * NT) * 4);
 #pragma unroll
         for (int k0 = 0; k0 < WN; k0 += WB) {
             uint4 w4[WB];
 #pragma unroll
-            for (int k = 0; k < WB; ++k) w4[k] = *(const uint4*)(Wb + (size_t)(tid + (k0 + k) * 256) * 8);
+            for (int k = 0; k < WB; ++k) {
+                const int pc = tid + (k0 + k) * NT;
+                w4[k] = pc < WTOT ? *(const uint4*)(Wb + (size_t)pc * 8) : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
             for (int k = 0; k < WB; ++k) {
-                const int e = (tid + (k0 + k) * 256) * 8, row = e / D, col = e % D;  // row = part * Fh + feature
-                *(uint4*)(Wl + row * (D + 8) + col) = w4[k];
+                const int pc = tid + (k0 + k) * NT;
+                const int e = pc * 8, row = e / D, col = e % D;  // row = part * Fh + feature
+                if (pc < WTOT) *(uint4*)(Wl + row * (D + 8) + col) = w4[k];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int k = 0; k < HN; ++k) {
-            const int i = tid + k * 256, dd = (i * 4) / F, f = (i * 4) % F;
+            const int i = tid + k * NT, dd = (i * 4) / F, f = (i * 4) % F;
             const float vv[4] = {hv4[k].x, hv4[k].y, hv4[k].z, hv4[k].w};
             uint16_t h[4], l[4];
 #pragma unroll
@@ -202,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             *(uint2*)(HhT + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
             *(uint2*)(HlT + o) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
         }
-        for (int i = tid; i < F; i += 256) {
+        for (int i = tid; i < F; i += NT) {
             const float x = ch.s()[i];
             const int o = perm_pos(i);
             sP[o] = x;
@@ -213,21 +293,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             sParts[F + o] = p2;
             sParts[2 * F + o] = bf16_bits(r1 - bf16_val(p2));
         }
-        for (int i = tid; i < cnt; i += 256) cposL[i] = ch.cpos()[i];
+        for (int i = tid; i < cnt; i += NT) cposL[i] = ch.cpos()[i];
+        if (tid == 0) misc[1] = 0;  // set once the leaving key's features are in LDS
     }
-    // query frags (columns r16 < G); the leaving key's row (wave 3, column 0) and
-    // its value rows dt * 16 + 4 qg .. + 3 (waves 0 and 3)
+    // query frags (read waves, columns r16 < G); the leaving key's row (last wave,
+    // column 0) and its value rows dt * 16 + 4 qg .. + 3 (wave 0 and the last wave)
     bf16x8 qf[DS];
     uint4 kEq[DS];
     uint2 vEq[DT];
     {
-        const bool le = hasE && (wave == 0 || wave == NW - 1);
+        const bool le = hasE && (wave == 0 || wave == LASTW);
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks)
-            kEq[ks] = (hasE && wave == NW - 1 && r16 == 0) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
+            kEq[ks] = (hasE && wave == LASTW && r16 == 0) ? *(const uint4*)(kE + ks * 32 + qg * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vEq[dt] = le ? *(const uint2*)(vE + dt * 16 + qg * 4) : make_uint2(0, 0);
-        const bool qv = r16 < G;
+        const bool qv = rd && r16 < G;
         const bf16* qp = (const bf16*)a.q + ((size_t)b * d.Hq + g * G + (qv ? r16 : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) {
@@ -236,14 +317,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
     __syncthreads();  // W parts and H in LDS
+    // the first group of keys (read waves) and the first cache tiles (management waves)
+    if (rd) {
+        if (g0 < ng) issue(g0);
+    } else if (scoreCache && bw < nT) {
+        tile_load(bw);
+    }
     // Error of P tiles of 16 candidates from their feature operands (bf16 hi, lo
     // parts bh, bl; candidate r16 of tile p) and 1 / d: n^T = H^T phi^T with H and phi
     // in hi/lo parts (hi.hi + lo.hi + hi.lo; the H operands are read once for all P
-    // tiles), e = |n / d - v|^2 (values vq[p] at rows dt * 16 + 4 qg .. + 3, cv[p]
-    // whether the column is a candidate)
+    // tiles), e = |n / d - v|^2 (values vq[p] at rows dt * 16 + 4 qg .. + 3)
     // (nout[p], if given, receives candidate r16's n at its rows dt * 16 + 4 qg .. + 3)
-    auto sre_core = [&](auto pTag, const bf16x8 (*bh)[FM], const bf16x8 (*bl)[FM], const float* inv, const bool* cv,
-                        const uint2 (*vq)[DT], float* e, float* const* nout = nullptr) {
+    auto sre_core = [&](auto pTag, const bf16x8 (*bh)[FM], const bf16x8 (*bl)[FM], const float* inv,
+                        const uint2 (*vqq)[DT], float* e, float* const* nout = nullptr) {
         constexpr int P = decltype(pTag)::value;
         float es[P];
 #pragma unroll
@@ -267,8 +353,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             }
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const float vv[4] = {__uint_as_float(vq[p][dt].x << 16), __uint_as_float(vq[p][dt].x & 0xffff0000u),
-                                     __uint_as_float(vq[p][dt].y << 16), __uint_as_float(vq[p][dt].y & 0xffff0000u)};
+                const float vv[4] = {__uint_as_float(vqq[p][dt].x << 16), __uint_as_float(vqq[p][dt].x & 0xffff0000u),
+                                     __uint_as_float(vqq[p][dt].y << 16), __uint_as_float(vqq[p][dt].y & 0xffff0000u)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float df = (acc[p][i] + acc2[p][i]) * inv[p] - vv[i];
@@ -306,243 +392,151 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
         return (dac[0] + dac[1]) + dac[2];
     };
-    // SRE of P tiles whose features are computed here from the key fragments kb[p]
-    auto sre_tiles = [&](auto pTag, const bf16x8 (*kb)[DS], const bool* cv, const uint2 (*vq)[DT], float* e,
-                         float* phi0 = nullptr,    // phi0: phi of candidate 0 of tile 0, natural order
-                         float* nd0 = nullptr) {   // nd0: n (D values) then d of candidate 0 of tile 0
-        constexpr int P = decltype(pTag)::value;
-        bf16x8 bh[P][FM], bl[P][FM];
-        float inv[P];
-        {
-            float x[P][F / 4];
-            phi_tiles<D, F, P>(Wl, kb, r16, qg, x);
-            if (phi0 && r16 == 0)
-#pragma unroll
-                for (int h = 0; h < F / 4; ++h) phi0[slot_feature(h, qg)] = x[0][h];
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-#pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    u16x8 uh, ul;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float xv = x[p][mf * 8 + j];
-                        const uint16_t h = bf16_bits(xv);
-                        uh[j] = h;
-                        ul[j] = bf16_bits(xv - bf16_val(h));
-                    }
-                    bh[p][mf] = __builtin_bit_cast(bf16x8, uh);
-                    bl[p][mf] = __builtin_bit_cast(bf16x8, ul);
-                }
-                const float dd = dot_s(bh[p], bl[p]);
-                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
-                if (nd0 && p == 0 && lane == 0) nd0[D] = dd;
-            }
-        }
-        float* nout[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) nout[p] = (nd0 && p == 0 && r16 == 0) ? nd0 : nullptr;
-        sre_core(pTag, bh, bl, inv, cv, vq, e, nout);
-    };
 
-    // Wave 3: phi of the leaving key (column 0 of a tile) and, when a pair must be
-    // folded, its SRE against the step-start state.  Meanwhile wave 0, the only wave
-    // that needs phi(q), computes it and the linear read O_lin^T = H^T phi(q)^T; the
-    // leaving key's share of the linear part is added once its features are in LDS.
-    const int nU = cnt + (hasE ? 1 : 0);
     floatx4 O[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mrun = 0.f, Zp = 0.f;
-    float xq[F / 4];  // wave 0: phi(q) of column r16, operand-slot order
-    float zq = 0.f;   // wave 0: s . phi(q)
-    if (wave == NW - 1) {
-        bf16x8 kb[1][DS];
+    const float tau = d.tau;
+    if (rd) {
+        if (wave == 0) {
+            // phi(q) for the query columns: z^T = W Q^T with W hi + lo, then the linear
+            // read O_lin^T = H^T phi(q)^T and s . phi(q)
+            float xq[F / 4];  // phi(q) of column r16, operand-slot order
+            float zq = 0.f;
+            floatx4 zt[Fh / 16];
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) kb[0][ks] = __builtin_bit_cast(bf16x8, kEq[ks]);
-        if (hasE && (nU > C || INC)) {  // (incremental decode: n, d of a key that may enter the cache)
-            const bool cv[1] = {r16 == 0};
-            uint2 vq[1][DT];
+            for (int ft = 0; ft < Fh / 16; ++ft) {
+                zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vq[0][dt] = vEq[dt];
-            float e[1];
-            sre_tiles(std::integral_constant<int, 1>{}, kb, cv, vq, e, phiE, INC ? nEL : nullptr);
-            if (lane == 0) esc[cnt] = e[0];
-        } else {
-            float x[1][F / 4];
-            phi_tiles<D, F, 1>(Wl, kb, r16, qg, x);
-            if (r16 == 0)
-#pragma unroll
-                for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
-        }
-    } else if (wave == 0) {
-        // phi(q) for the query columns: z^T = W Q^T with W hi + lo
-        floatx4 zt[Fh / 16];
-#pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft) {
-            zt[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                const int o = (ft * 16 + r16) * (D + 8) + ks * 32 + qg * 8;
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), qf[ks], zt[ft], 0, 0, 0);
-                zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * (D + 8) + o), qf[ks], zt[ft], 0, 0, 0);
+                for (int ks = 0; ks < DS; ++ks) {
+                    const int o = (ft * 16 + r16) * (D + 8) + ks * 32 + qg * 8;
+                    zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + o), qf[ks], zt[ft], 0, 0, 0);
+                    zt[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(Wl + Fh * (D + 8) + o), qf[ks], zt[ft], 0, 0, 0);
+                }
             }
-        }
-        float zmax = -INFINITY, zmin = INFINITY;
+            float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft)
+            for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
-        zmax = quad_max(zmax);
-        zmin = quad_min(zmin);
-        float sp = 0.f, sn = 0.f;
+                for (int i = 0; i < 4; ++i) { zmax = fmaxf(zmax, zt[ft][i]); zmin = fminf(zmin, zt[ft][i]); }
+            zmax = quad_max(zmax);
+            zmin = quad_min(zmin);
+            float sp = 0.f, sn = 0.f;
 #pragma unroll
-        for (int ft = 0; ft < Fh / 16; ++ft)
+            for (int ft = 0; ft < Fh / 16; ++ft)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e1 = __expf(zt[ft][i] - zmax), e2 = __expf(zmin - zt[ft][i]);
-                xq[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
-                xq[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
-                sp += e1;
-                sn += e2;
+                for (int i = 0; i < 4; ++i) {
+                    const float e1 = __expf(zt[ft][i] - zmax), e2 = __expf(zmin - zt[ft][i]);
+                    xq[(ft >> 1) * 8 + (ft & 1) * 4 + i] = e1;
+                    xq[Fh / 4 + (ft >> 1) * 8 + (ft & 1) * 4 + i] = e2;
+                    sp += e1;
+                    sn += e2;
+                }
+            sp = quad_sum(sp);
+            sn = quad_sum(sn);
+            const float isp = 1.f / sp, isn = 1.f / sn;
+            bf16x8 pf[FM];
+#pragma unroll
+            for (int mf = 0; mf < FM; ++mf) {
+                u16x8 u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int hidx = mf * 8 + j;
+                    xq[hidx] *= hidx < Fh / 4 ? isp : isn;
+                    u[j] = bf16_bits(xq[hidx]);
+                    zq += xq[hidx] * sP[mf * 32 + qg * 8 + j];  // operand position of this feature
+                }
+                pf[mf] = __builtin_bit_cast(bf16x8, u);
             }
-        sp = quad_sum(sp);
-        sn = quad_sum(sn);
-        const float isp = 1.f / sp, isn = 1.f / sn;
-        bf16x8 pf[FM];
+            zq = quad_sum(zq);
 #pragma unroll
-        for (int mf = 0; mf < FM; ++mf) {
-            u16x8 u;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int hidx = mf * 8 + j;
-                xq[hidx] *= hidx < Fh / 4 ? isp : isn;
-                u[j] = bf16_bits(xq[hidx]);
-                zq += xq[hidx] * sP[mf * 32 + qg * 8 + j];  // operand position of this feature
+                for (int mf = 0; mf < FM; ++mf)
+                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(HhT + (dt * 16 + r16) * HP + mf * 32 + qg * 8),
+                                                                    pf[mf], O[dt], 0, 0, 0);
+            // the leaving key's linear weight kappa = phi(q) . phi(k_E) per query column;
+            // kappa * v_E joins the linear part (weight e^-M, M floored at 0).  Its
+            // features come from the last wave through LDS: wait for its flag (a bounded
+            // poll; the last wave sets the flag without waiting for anything)
+            {
+                int it = 0;
+                while (__hip_atomic_load(&misc[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 && it < (1 << 22)) {
+                    __builtin_amdgcn_s_sleep(1);
+                    ++it;
+                }
+                if (it >= (1 << 22) && lane == 0)
+                    __hip_atomic_store(&((StateHeader*)a.state)->fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             }
-            pf[mf] = __builtin_bit_cast(bf16x8, u);
-        }
-        zq = quad_sum(zq);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            float kap = 0.f;
 #pragma unroll
             for (int mf = 0; mf < FM; ++mf)
-                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(HhT + (dt * 16 + r16) * HP + mf * 32 + qg * 8),
-                                                                pf[mf], O[dt], 0, 0, 0);
-    }
-    __syncthreads();  // phi of the leaving key in LDS
-    if (wave == 0) {
-        // the leaving key's linear weight kappa = phi(q) . phi(k_E) per query column;
-        // kappa * v_E joins the linear part (weight e^-M, M floored at 0)
-        float kap = 0.f;
 #pragma unroll
-        for (int mf = 0; mf < FM; ++mf)
+                for (int j = 0; j < 8; ++j) kap += xq[mf * 8 + j] * phiE[(2 * mf + (j >> 2)) * 16 + qg * 4 + (j & 3)];
+            kap = quad_sum(kap);
+            if (!hasE) kap = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) kap += xq[mf * 8 + j] * phiE[(2 * mf + (j >> 2)) * 16 + qg * 4 + (j & 3)];
-        kap = quad_sum(kap);
-        if (!hasE) kap = 0.f;
+            for (int dt = 0; dt < DT; ++dt) {
+                const float vv[4] = {__uint_as_float(vEq[dt].x << 16), __uint_as_float(vEq[dt].x & 0xffff0000u),
+                                     __uint_as_float(vEq[dt].y << 16), __uint_as_float(vEq[dt].y & 0xffff0000u)};
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const float vv[4] = {__uint_as_float(vEq[dt].x << 16), __uint_as_float(vEq[dt].x & 0xffff0000u),
-                                 __uint_as_float(vEq[dt].y << 16), __uint_as_float(vEq[dt].y & 0xffff0000u)};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) O[dt][i] += kap * vv[i];
-        }
-        Zp = qg == 0 ? zq + kap : 0.f;
-    }
-
-    // ---- keys: window [ws0, t] then cache slots; blocks of 128, 32 per wave ----
-    const int64_t ws0 = t - w + 1 > 0 ? t - w + 1 : 0;
-    const int nWin = w > 0 ? (int)(t - ws0 + 1) : 0;
-    const int nK = nWin + cnt;
-    // row of key kidx (0 <= kidx < nK): window position ws0 + kidx (ring slot
-    // (ws0 + kidx) mod w, the newest being this step's token), then cache slot
-    // kidx - nWin; chosen by selects so that a block's loads issue together
-    const int rs0 = w > 0 ? (int)(ws0 % w) : 0;
-    auto key_row = [&](int kidx, bool v) -> const bf16* {
-        int slot = rs0 + kidx;
-        slot = slot >= w ? slot - w : slot;
-        const bf16* pw = (v ? ch.ring_v<bf16>() : ch.ring_k<bf16>()) + (size_t)slot * D;
-        const bf16* pc = (v ? ch.cache_v<bf16>() : ch.cache_k<bf16>()) + (ptrdiff_t)(kidx - nWin) * D;
-        const bf16* pn = v ? vnew : knew;
-        return kidx < nWin ? (kidx == nWin - 1 ? pn : pw) : pc;
-    };
-    const float tau = d.tau;
-
-    const int nblk = (nK + KBL - 1) / KBL;
-    // Block bi + 1's key fragments and value rows load while block bi is scored; rows
-    // past nK load the last key and are zeroed.  A wave takes keys base + wave * KW +
-    // tt * 16 + r16 as MFMA fragments straight from memory (a lane's 16 bytes are
-    // contiguous in the key row).
-    constexpr int VN = (KBL / 2) * (D / 8) / 256;
-    static_assert((KBL / 2) * (D / 8) % 256 == 0, "V units cover the key block exactly");
-    uint4 kq[2][DS], vq0[VN], vq1[VN];
-    auto issue = [&](int base) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int kidx = base + wave * KW + tt * 16 + r16;
-            const bf16* kr = key_row(kidx < nK ? kidx : nK - 1, false);
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) kq[tt][ks] = *(const uint4*)(kr + ks * 32 + qg * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < VN; ++k) {
-            const int idx = tid + k * 256, k0 = base + 2 * (idx % (KBL / 2)), un = idx / (KBL / 2);
-            vq0[k] = *(const uint4*)(key_row(k0 < nK ? k0 : nK - 1, true) + un * 8);
-            vq1[k] = *(const uint4*)(key_row(k0 + 1 < nK ? k0 + 1 : nK - 1, true) + un * 8);
-        }
-    };
-    if (nK > 0) issue(0);
-    for (int bi = 0; bi < nblk; ++bi) {
-        const int base = bi * KBL;
-        __syncthreads();  // previous block consumed
-        uint4 kcur[2][DS];  // this block's fragments (kq is refilled below)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) kcur[tt][ks] = kq[tt][ks];
-#pragma unroll
-        for (int k = 0; k < VN; ++k) {
-            // a wave covers 64 key pairs of one value unit: each transposed store puts its
-            // lanes on distinct dwords of one row (units 8 rows apart share an LDS bank)
-            const int idx = tid + k * 256, pr = idx % (KBL / 2), un = idx / (KBL / 2);
-            const int k0 = base + 2 * pr, k1 = k0 + 1;
-            const uint4 v0 = k0 < nK ? vq0[k] : make_uint4(0, 0, 0, 0);
-            const uint4 v1 = k1 < nK ? vq1[k] : make_uint4(0, 0, 0, 0);
-            const int kc = (2 * pr / KW) * KW + key_perm((2 * pr) % KW);
-            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-                const uint32_t hi = (w1[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-                *(uint32_t*)(stVT + (un * 8 + j) * VP + kc) = lo | (hi << 16);
+                for (int i = 0; i < 4; ++i) O[dt][i] += kap * vv[i];
             }
+            Zp = qg == 0 ? zq + kap : 0.f;
         }
-        if (bi + 1 < nblk) issue(base + KBL);
-        lds_sync();  // V^T staged; the next block's loads stay in flight
-        // this wave's 32 keys: base + wave*32 + tt*16 + r16
-        const int kb0 = base + wave * KW;
-        if (kb0 >= nK) continue;
-        floatx4 sT[2];
-        bf16x8 kfr[2][DS];
+
+        // ---- this wave's groups of 32 keys: the next group loads while the current
+        //      one is scored; V^T is staged in the wave's own 32 columns of the staging
+        //      area, so no other wave is waited for ----
+        for (int gg = g0; gg < ng; gg += NA) {
+            const int base = gg * KW;
+            uint4 kcur[2][DS], va[VNW], vb[VNW];  // this group's rows (kq, vqa, vqb are refilled below)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            sT[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                kfr[tt][ks] = __builtin_bit_cast(bf16x8, kb0 + tt * 16 + r16 < nK ? kcur[tt][ks] : make_uint4(0, 0, 0, 0));
-                sT[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[tt][ks], qf[ks], sT[tt], 0, 0, 0);
+                for (int ks = 0; ks < DS; ++ks) kcur[tt][ks] = base + tt * 16 + r16 < nK ? kq[tt][ks] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < VNW; ++j) {
+                va[j] = base + 2 * r16 < nK ? vqa[j] : make_uint4(0, 0, 0, 0);
+                vb[j] = base + 2 * r16 + 1 < nK ? vqb[j] : make_uint4(0, 0, 0, 0);
             }
-        }
-        // online softmax for the query column r16 over the lane's 8 keys
-        {
+            if (gg + NA < ng) issue(gg + NA);
+            // V^T of the group: LDS runs one wave's instructions in order, so these stores
+            // land after the previous group's reads of the same columns and before this
+            // group's reads (the asm keeps the compiler from moving LDS accesses across)
+            asm volatile("" ::: "memory");
+            const int kc = wave * KW + key_perm(2 * r16);
+#pragma unroll
+            for (int j = 0; j < VNW; ++j) {
+                const int un = qg + 4 * j;
+                const uint32_t w0[4] = {va[j].x, va[j].y, va[j].z, va[j].w}, w1[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    *(uint32_t*)(stVT + (un * 8 + e) * VP + kc) = lo | (hi << 16);
+                }
+            }
+            lds_wait();
+            asm volatile("" ::: "memory");
+            floatx4 sT[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                sT[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DS; ++ks)
+                    sT[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kcur[tt][ks]), qf[ks], sT[tt], 0, 0, 0);
+            }
+            // online softmax for the query column r16 over the lane's 8 keys
             float lg[8];
             bool ok[8];
             float bmax = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int tt = j >> 2, i = j & 3;
-                const int kidx = kb0 + tt * 16 + qg * 4 + i;
+                const int kidx = base + tt * 16 + qg * 4 + i;
                 ok[j] = kidx < nK && r16 < G;
                 lg[j] = tau * sT[tt][i];
                 if (ok[j]) bmax = fmaxf(bmax, lg[j]);
@@ -567,41 +561,127 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
                 O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(stVT + (dt * 16 + r16) * VP + wave * KW + qg * 8),
                                                                 pb, O[dt], 0, 0, 0);
         }
-    }
-
-    // the MFMA SRE pass over the cache runs: to choose a victim, or (incremental decode)
-    // to compute the stored n, d of every cached pair afresh; otherwise the incremental
-    // decode scores a full cache from the stored n, d
-    const bool scoreCache = INC ? (!incValid && cnt > 0) : (hasE && nU > C);
-    const bool storedScores = INC && incValid && hasE && nU > C;
-    const int nT = (cnt + 15) / 16;
-    // features of the cached keys come from the state (hi | lo rows in operand order)
-    uint4 fq[2][2 * FM];
-    uint2 vq[2][DT];
-    auto tile_load = [&](int p, int tt) {
-        const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
-        const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
-        const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
+    } else {
+        // ---- management waves ----
+        if (wave == LASTW) {
+            // phi of the leaving key (column 0 of a tile), handed to wave 0 through LDS,
+            // then, when a pair must be folded (or, incremental decode, the key may enter
+            // the cache with its n, d), its SRE against the step-start state
+            bf16x8 kb[1][DS];
 #pragma unroll
-        for (int mf = 0; mf < FM; ++mf) {
-            fq[p][mf] = *(const uint4*)(pr + mf * 32);
-            fq[p][FM + mf] = *(const uint4*)(pr + F + mf * 32);
+            for (int ks = 0; ks < DS; ++ks) kb[0][ks] = __builtin_bit_cast(bf16x8, kEq[ks]);
+            float x[1][F / 4];
+            phi_tiles<D, F, 1>(Wl, kb, r16, qg, x);
+            if (r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0) __hip_atomic_store(&misc[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (hasE && (foldStep || INC)) {
+                bf16x8 bh[1][FM], bl[1][FM];
+#pragma unroll
+                for (int mf = 0; mf < FM; ++mf) {
+                    u16x8 uh, ul;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float xv = x[0][mf * 8 + j];
+                        const uint16_t h = bf16_bits(xv);
+                        uh[j] = h;
+                        ul[j] = bf16_bits(xv - bf16_val(h));
+                    }
+                    bh[0][mf] = __builtin_bit_cast(bf16x8, uh);
+                    bl[0][mf] = __builtin_bit_cast(bf16x8, ul);
+                }
+                const float dd = dot_s(bh[0], bl[0]);
+                const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
+                if (INC && lane == 0) nEL[D] = dd;
+                uint2 vqq[1][DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vqq[0][dt] = vEq[dt];
+                float* nout[1] = {(INC && r16 == 0) ? nEL : nullptr};
+                float e[1];
+                sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, vqq, e, nout);
+                if (lane == 0) esc[cnt] = e[0];
+            }
         }
+        // the cache in tiles of 16 slots dealt to the management waves in turn; each
+        // tile's feature and value rows load while the previous tile is scored
+        if (scoreCache) {
+            for (int t0 = bw; t0 < nT; t0 += NB) {
+                bf16x8 bh[1][FM], bl[1][FM];
+                uint2 vv[1][DT];
+                // (slots past the count are scored as stored -- zero or an earlier
+                // pair's finite row -- and their errors are not kept)
+                const bool cv = t0 * 16 + r16 < cnt;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vq[p][dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
-    };
-    // the wave's tiles wave, wave + NW, ... two at a time; the first two load while
-    // the attention parts are merged, the next two while the current two are scored
-    if (scoreCache && wave < nT) tile_load(0, wave);
-    if (scoreCache && wave + NW < nT) tile_load(1, wave + NW);
+                for (int mf = 0; mf < FM; ++mf) {
+                    bh[0][mf] = __builtin_bit_cast(bf16x8, fq[mf]);
+                    bl[0][mf] = __builtin_bit_cast(bf16x8, fq[FM + mf]);
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vv[0][dt] = vq[dt];
+                if (t0 + NB < nT) tile_load(t0 + NB);
+                const float dd = dot_s(bh[0], bl[0]);
+                const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
+                float* nout[1] = {nullptr};
+                if (INC && cv) {  // the stored n, d of this cached pair, computed afresh
+                    const int slot = t0 * 16 + r16;
+                    nout[0] = ch.cn() + (size_t)slot * D;
+                    if (qg == 0) ch.cd()[slot] = dd;
+                }
+                float e[1];
+                sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, vv, e, nout);
+                if (qg == 0 && cv) esc[t0 * 16 + r16] = e[0];
+            }
+        }
+        if constexpr (INC) {
+            if (storedScores) {
+                // e = |n / d - v|^2 from the stored n, d: 16 lanes per cached pair, D / 16
+                // values each (one 16-lane group reads a contiguous row)
+                constexpr int DPL = D / 16;
+                const int sub = lane & 15;
+                for (int u = ((tid - NA * 64) >> 4); u < cnt; u += NB * 4) {
+                    const float dd = ch.cd()[u];
+                    const float inv = dd > 0.f ? 1.f / dd : 0.f;
+                    const float* nr = ch.cn() + (size_t)u * D + sub * DPL;
+                    const bf16* vr = ch.cache_v<bf16>() + (size_t)u * D + sub * DPL;
+                    float e = 0.f;
+#pragma unroll
+                    for (int j = 0; j < DPL; j += 4) {
+                        float nv[4], vv[4];
+                        load4(nr + j, nv);
+                        load4(vr + j, vv);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float df = nv[i] * inv - vv[i];
+                            e += df * df;
+                        }
+                    }
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
+                    if (sub == 0) esc[u] = e;
+                }
+            }
+        }
+    }
+    // the read's parts are final and the staging area is free; all SRE in LDS (the
+    // incremental decode's fresh n, d stores are also visible to the whole workgroup)
+    if constexpr (INC) __syncthreads();
+    else lds_sync();
 
-    // ---- merge the waves' softmax parts, add the linear part, store ----
-    // (LDS-only barriers: the first cache tiles' loads stay in flight)
-    lds_sync();  // staging area becomes the merge area
-    {
-        float* mM = mrg;                 // [NW][16]
-        float* mZ = mrg + NW * 16;       // [NW][16]
-        float* mO = mrg + 2 * NW * 16;   // [NW][D][16]
+    // ---- merge the read waves' softmax parts; choose the victim and fetch its row ----
+    constexpr int HN = D * F / 4 / NT;  // float4 of H per thread for the fold
+    float4 h4[HN];
+    float* Hd = ch.H();
+    if (foldStep) {
+        // H (fp32) for the fold is requested before the victim is known
+#pragma unroll
+        for (int k = 0; k < HN; ++k) h4[k] = *(const float4*)(Hd + (size_t)(tid + k * NT) * 4);
+    }
+    float* mM = mrg;                 // [NA][16]
+    float* mZ = mrg + NA * 16;       // [NA][16]
+    float* mO = mrg + 2 * NA * 16;   // [NA][D][16]
+    if (rd) {
         float Z = Zp;
         Z = quad_sum(Z);
         if (qg == 0) { mM[wave * 16 + r16] = mrun; mZ[wave * 16 + r16] = Z; }
@@ -609,151 +689,63 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mO[(wave * D + dt * 16 + qg * 4 + i) * 16 + r16] = O[dt][i];
-        lds_sync();
-        for (int idx = tid; idx < G * D; idx += 256) {
-            const int col = idx / D, dd = idx % D;
-            float M = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mM[ww * 16 + col]);
-            float num = 0.f, den = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float sc = __expf(mM[ww * 16 + col] - M);
-                num += sc * mO[(ww * D + dd) * 16 + col];
-                den += sc * mZ[ww * 16 + col];
-            }
-            ((bf16*)a.out)[((size_t)b * d.Hq + g * G + col) * D + dd] = from_f32<bf16>(num / den);
+    } else if (foldStep && wave == NA) {
+        // lowest SRE, newest position on a tie: minimise (bits(e), ~pos)
+        unsigned long long best = ~0ull;
+        for (int u = lane; u < nU; u += 64) {
+            const uint32_t pos = u < cnt ? (uint32_t)cposL[u] : (uint32_t)pE;
+            const unsigned long long key = ((unsigned long long)__float_as_uint(esc[u]) << 32) | (0xffffffffu - pos);
+            best = key < best ? key : best;
         }
-    }
-
-    // ---- SRE of the cached pairs (only when a pair must be folded; the leaving
-    //      pair's was scored with its phi): the cache in tiles of 16 slots dealt to
-    //      the waves in turn; each tile's key and value rows are loaded while the
-    //      previous tiles are scored ----
-    if (scoreCache) {
-        for (int t0 = wave; t0 < nT; t0 += 2 * NW) {
-            const int tl[2] = {t0, t0 + NW};
-            bf16x8 bh[2][FM], bl[2][FM];
-            float inv[2];
-            bool cv[2];
-            uint2 vv[2][DT];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                cv[p] = tl[p] * 16 + r16 < cnt;
-#pragma unroll
-                // (slots past the count are scored as stored -- zero or an earlier
-                // pair's finite row -- and their errors are not kept)
-                for (int mf = 0; mf < FM; ++mf) {
-                    bh[p][mf] = __builtin_bit_cast(bf16x8, fq[p][mf]);
-                    bl[p][mf] = __builtin_bit_cast(bf16x8, fq[p][FM + mf]);
-                }
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vv[p][dt] = vq[p][dt];
-            }
-            if (t0 + 2 * NW < nT) tile_load(0, t0 + 2 * NW);
-            if (t0 + 3 * NW < nT) tile_load(1, t0 + 3 * NW);
-            float* nout[2] = {nullptr, nullptr};
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const float dd = dot_s(bh[p], bl[p]);
-                inv[p] = dd > 0.f ? 1.f / dd : 0.f;
-                if (INC && cv[p]) {  // the stored n, d of this cached pair, computed afresh
-                    const int slot = tl[p] * 16 + r16;
-                    nout[p] = ch.cn() + (size_t)slot * D;
-                    if (qg == 0) ch.cd()[slot] = dd;
-                }
-            }
-            float e[2];
-            if (tl[1] < nT) sre_core(std::integral_constant<int, 2>{}, bh, bl, inv, cv, vv, e, nout);  // wave-uniform
-            else sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, cv, vv, e, nout);
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-                if (tl[p] < nT && qg == 0 && cv[p]) esc[tl[p] * 16 + r16] = e[p];
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned long long other = __shfl_xor(best, o, 64);
+            best = other < best ? other : best;
         }
-    }
-    if constexpr (INC) {
-        if (storedScores) {
-            // e = |n / d - v|^2 from the stored n, d: 16 lanes per cached pair, D / 16
-            // values each (one 16-lane group reads a contiguous row)
-            constexpr int DPL = D / 16;
-            const int sub = lane & 15;
-            for (int u = (tid >> 4); u < cnt; u += 16) {
-                const float dd = ch.cd()[u];
-                const float inv = dd > 0.f ? 1.f / dd : 0.f;
-                const float* nr = ch.cn() + (size_t)u * D + sub * DPL;
-                const bf16* vr = ch.cache_v<bf16>() + (size_t)u * D + sub * DPL;
-                float e = 0.f;
-#pragma unroll
-                for (int j = 0; j < DPL; j += 4) {
-                    float nv[4], vv[4];
-                    load4(nr + j, nv);
-                    load4(vr + j, vv);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float df = nv[i] * inv - vv[i];
-                        e += df * df;
-                    }
-                }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
-                if (sub == 0) esc[u] = e;
+        const uint32_t pos = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
+        int vi = cnt;
+        for (int u = lane; u < cnt; u += 64)
+            if ((uint32_t)cposL[u] == pos) vi = u;
+        for (int o = 32; o > 0; o >>= 1) vi = min(vi, __shfl_xor(vi, o, 64));
+        if (lane == 0) misc[0] = vi;
+        // the folded pair: its stored feature row (hi + lo) or the leaving key's
+        // features, and its value
+        if (vi < cnt) {
+            const uint16_t* pr = ch.cphi() + (size_t)vi * 2 * F;
+            for (int f = lane; f < F; f += 64) {
+                const int q = perm_pos(f);
+                phiF[f] = bf16_val(pr[q]) + bf16_val(pr[F + q]);
+                if (INC) phiFop[q] = phiF[f];
             }
-        }
+        } else
+            for (int f = lane; f < F; f += 64) {
+                phiF[f] = phiE[f];
+                if (INC) phiFop[perm_pos(f)] = phiE[f];
+            }
+        const bf16* vr = vi < cnt ? ch.cache_v<bf16>() + (size_t)vi * D : vE;
+        for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
     }
-    __syncthreads();
+    lds_sync();  // merge parts, victim and its rows in LDS (H stays in flight)
+    for (int idx = tid; idx < G * D; idx += NT) {
+        const int col = idx / D, dd = idx % D;
+        float M = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NA; ++ww) M = fmaxf(M, mM[ww * 16 + col]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NA; ++ww) {
+            const float sc = __expf(mM[ww * 16 + col] - M);
+            num += sc * mO[(ww * D + dd) * 16 + col];
+            den += sc * mZ[ww * 16 + col];
+        }
+        ((bf16*)a.out)[((size_t)b * d.Hq + g * G + col) * D + dd] = from_f32<bf16>(num / den);
+    }
     int victim = -1;
-    if (hasE && nU > C) {
-        // H (fp32) for the fold is requested before the victim is known
-        float* Hd = ch.H();
-        constexpr int HN = D * F / 4 / 256;  // float4 per thread
-        float4 h4[HN];
-#pragma unroll
-        for (int k = 0; k < HN; ++k) h4[k] = *(const float4*)(Hd + (size_t)(tid + k * 256) * 4);
-        if (wave == 0) {
-            // lowest SRE, newest position on a tie: minimise (bits(e), ~pos)
-            unsigned long long best = ~0ull;
-            for (int u = lane; u < nU; u += 64) {
-                const uint32_t pos = u < cnt ? (uint32_t)cposL[u] : (uint32_t)pE;
-                const unsigned long long key = ((unsigned long long)__float_as_uint(esc[u]) << 32) | (0xffffffffu - pos);
-                best = key < best ? key : best;
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const unsigned long long other = __shfl_xor(best, o, 64);
-                best = other < best ? other : best;
-            }
-            const uint32_t pos = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
-            int vi = cnt;
-            for (int u = lane; u < cnt; u += 64)
-                if ((uint32_t)cposL[u] == pos) vi = u;
-            for (int o = 32; o > 0; o >>= 1) vi = min(vi, __shfl_xor(vi, o, 64));
-            if (lane == 0) misc[0] = vi;
-        }
-        lds_sync();  // (LDS-only barriers up to the fold: H stays in flight)
+    if (foldStep) {
+        // H += phi v^T, s += phi
         victim = misc[0];
-        // phi of the folded key (wave 0, column 0 of a tile) and its value (wave 1),
-        // then H += phi v^T, s += phi
-        if (wave == 0) {
-            // the folded key's features: its stored row (hi + lo), or the leaving key's
-            if (victim < cnt) {
-                const uint16_t* pr = ch.cphi() + (size_t)victim * 2 * F;
-                for (int f = lane; f < F; f += 64) {
-                    const int q = perm_pos(f);
-                    phiF[f] = bf16_val(pr[q]) + bf16_val(pr[F + q]);
-                    if (INC) phiFop[q] = phiF[f];
-                }
-            } else
-                for (int f = lane; f < F; f += 64) {
-                    phiF[f] = phiE[f];
-                    if (INC) phiFop[perm_pos(f)] = phiE[f];
-                }
-        } else if (wave == 1) {
-            const bf16* vr = victim < cnt ? ch.cache_v<bf16>() + (size_t)victim * D : vE;
-            for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
-        }
-        lds_sync();
 #pragma unroll
         for (int k = 0; k < HN; ++k) {
-            const int i = (tid + k * 256) * 4, dd = i / F, f = i % F;
+            const int i = (tid + k * NT) * 4, dd = i / F, f = i % F;
             const float vv = xrow[dd];
             h4[k].x += vv * phiF[f];
             h4[k].y += vv * phiF[f + 1];
@@ -761,20 +753,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
             h4[k].w += vv * phiF[f + 3];
             *(float4*)(Hd + i) = h4[k];
         }
-        for (int f = tid; f < F; f += 256) ch.s()[f] += phiF[f];
+        for (int f = tid; f < F; f += NT) ch.s()[f] += phiF[f];
     }
 
     if constexpr (INC) {
         // ---- stored n, d after this step: every cached pair that stays gains the folded
         //      pair's share, kappa = phi(k) . phi(k_f) times [v_f; 1] (H += phi_f v_f^T and
         //      s += phi_f leave n = H^T phi(k), d = s . phi(k) exactly that much larger);
-        //      a leaving key that enters the cache brings its own n, d (wave 3 computed
-        //      them against the step-start state) plus its share of the fold ----
-        const bool folded = hasE && nU > C;
-        if (folded) {
+        //      a leaving key that enters the cache brings its own n, d (the last wave
+        //      computed them against the step-start state) plus its share of the fold ----
+        if (foldStep) {
             constexpr int PPL = F / 16, DPL = D / 16;
             const int sub = lane & 15;
-            for (int u = (tid >> 4); u < cnt; u += 16) {
+            for (int u = (tid >> 4); u < cnt; u += NT / 16) {
                 if (u == victim) continue;  // (the whole 16-lane group)
                 const uint16_t* pr = ch.cphi() + (size_t)u * 2 * F + sub * PPL;
                 float kk = 0.f;
@@ -807,11 +798,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         const int enter = !hasE ? -1 : (nU <= C ? cnt : (victim < cnt ? victim : -1));
         if (enter >= 0 && wave == 0) {
             float ke = 0.f;
-            if (folded) {
+            if (foldStep) {
                 for (int f = lane; f < F; f += 64) ke += phiE[f] * phiF[f];
                 ke = wave_sum(ke);
             }
-            for (int j = lane; j < D; j += 64) ch.cn()[(size_t)enter * D + j] = nEL[j] + (folded ? ke * xrow[j] : 0.f);
+            for (int j = lane; j < D; j += 64) ch.cn()[(size_t)enter * D + j] = nEL[j] + (foldStep ? ke * xrow[j] : 0.f);
             if (lane == 0) ch.cd()[enter] = nEL[D] + ke;
         }
     }
@@ -826,12 +817,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         else if (victim < cnt) slot = victim;
     }
     if (slot >= 0) {
-        for (int j = tid; j < D; j += 256) {
+        for (int j = tid; j < D; j += NT) {
             ch.cache_k<bf16>()[(size_t)slot * D + j] = kE[j];
             ch.cache_v<bf16>()[(size_t)slot * D + j] = vE[j];
         }
         uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F;  // its features: hi | lo, operand order
-        for (int f = tid; f < F; f += 256) {
+        for (int f = tid; f < F; f += NT) {
             const float x = phiE[f];
             const uint16_t h = bf16_bits(x);
             pr[perm_pos(f)] = h;
@@ -839,7 +830,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_bf16(Args a)
         }
     }
     if (w > 0)
-        for (int j = tid; j < D; j += 256) {
+        for (int j = tid; j < D; j += NT) {
             ch.ring_k<bf16>()[(size_t)rs * D + j] = knew[j];
             ch.ring_v<bf16>()[(size_t)rs * D + j] = vnew[j];
         }
