@@ -406,6 +406,26 @@ def copy_calibration(nbytes=1 << 30):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def copy_bandwidth(nbytes=1 << 30, reps=5):
+    """Practical HBM ceiling on this GPU: a plain 1 GiB device-to-device copy (torch's copy
+    kernel), bytes read + written per second, timed with events over `reps` copies."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1000.0 / reps
+    del a, b
+    return {"gbs": 2 * nbytes / sec / 1e9, "bytes_per_copy": 2 * nbytes,
+            "what": "1 GiB device-to-device copy (read + write), the practical ceiling beside the 8 TB/s peak"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,8 +508,11 @@ def main():
         "warm": {"ms_per_step": pre["warm"]["ms_per_step"], "kernel_us": pre["warm"]["kernel_us"],
                  "value": pre["tokens"] / (pre["warm"]["ms_per_step"] / 1000.0)},
     }
+    res["hbm_copy"] = copy_bandwidth()
     if not args.no_decode:
         res["decode"] = bench_decode(I.WORKLOADS[4], args.decode_steps, args.warmup)
+        for part in (res["decode"]["roofline"], res["decode"]["warm"]["roofline"]):
+            part["frac_of_copy"] = part["achieved"] / res["hbm_copy"]["gbs"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, I.WORKLOADS[4])
     print(json.dumps(res), flush=True)
