@@ -141,7 +141,8 @@ typedef struct {
  * (sequence, KV head) the three memories of the summary's "Methodologie:
  * LoLA" section -- the sliding window (ring of the last `window` keys and
  * values), the sparse cache (positions, keys, values, and for bf16 io the
- * feature rows of the cached keys) and the recurrent state H [F][D] f32,
+ * feature-map pre-activations z = W k of the cached keys) and the recurrent
+ * state H [F][D] f32,
  * s [F] f32 -- plus the tokens seen.  The size does not grow with the
  * sequence length.  0 if the config or batch is not supported. */
 size_t lola_state_bytes(const lola_config* cfg, int32_t batch);

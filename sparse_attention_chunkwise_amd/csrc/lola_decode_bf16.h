@@ -11,14 +11,14 @@
 //             "Inferentiestrategie", step 4).
 //   manage -- the SRE equation ("Het Self-Recall Error (SRE) Mechanisme") for
 //             every cached key and the leaving key against the step-start
-//             state: the cached keys' features come from their stored bf16
-//             hi/lo rows (written when each key entered the cache), the
-//             leaving key's are computed, phi(k) = [softmax(W k); softmax(-W k)]
-//             by MFMA with W in three bf16 parts; n^T = H^T phi^T with H and
+//             state: the cached keys' features are recomputed from their
+//             stored z = W k (written when each key entered the cache: half the
+//             bytes of stored hi/lo feature rows), phi(k) = [softmax(z); softmax(-z)];
+//             the leaving key's z is computed by MFMA with W in three bf16 parts; n^T = H^T phi^T with H and
 //             phi in bf16 hi/lo parts, d = phi . s (s in three bf16 parts); then the pair with the
 //             lowest SRE (newest on a tie) is folded into H, s by one outer
 //             product when the candidates exceed the capacity, and the leaving
-//             key takes its cache slot with its feature row.
+//             key takes its cache slot with its z.
 #pragma once
 
 #include <type_traits>
@@ -30,7 +30,7 @@ namespace lola {
 constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
 
 struct DecSmem {
-    size_t HhT, HlT, Wl, sP, sParts, cposL, esc, phiE, phiF, xrow, stVT, nE, phiFop, misc, total;
+    size_t HhT, HlT, Wl, sP, sParts, cposL, esc, phiE, phiF, xrow, stVT, nE, zE, misc, total;
 };
 
 // The two arrays sized by the cache capacity come last: every other offset is a
@@ -51,7 +51,7 @@ __host__ __device__ constexpr DecSmem dec_smem(int C)
     m.xrow = off;  off += align_up(sizeof(float) * D, 16);
     m.stVT = off;  off += align_up(sizeof(uint16_t) * (size_t)D * (kDecBlock + 8), 16);
     m.nE = off;    off += align_up(sizeof(float) * (D + 4), 16);   // incremental decode: n, d of the leaving key
-    m.phiFop = off; off += align_up(sizeof(float) * F, 16);       // incremental decode: folded phi, operand order
+    m.zE = off;    off += align_up(sizeof(float) * (F / 2), 16);  // z = W k of the leaving key
     m.misc = off;  off += align_up(sizeof(int) * 16, 16);
     m.cposL = off; off += align_up(sizeof(int) * (size_t)Cp, 16);
     m.esc = off;   off += align_up(sizeof(float) * (size_t)(Cp + 1), 16);
@@ -59,18 +59,15 @@ __host__ __device__ constexpr DecSmem dec_smem(int C)
     return m;
 }
 
-// phi = [softmax(W k); softmax(-W k)] of P tiles of 16 keys (key r16 of tile p in
-// column r16 of kb[p]): z^T = W K^T by MFMA with W in three bf16 parts (exact
-// products against bf16 keys, fp32 sums; the W operands are read once for all P
-// tiles), then one softmax per half over the features.  x[p][h] is the feature
-// of operand slot h: slot h = 8 mf + j holds feature 16 (2 mf + j / 4) + 4 qg + j % 4
-// (positive half for mf < F / 64).
+// z^T = W K^T of P tiles of 16 keys (key r16 of tile p in column r16 of kb[p]) by
+// MFMA with W in three bf16 parts (exact products against bf16 keys, fp32 sums; the
+// W operands are read once for all P tiles): lane (r16, qg) gets features
+// ft * 16 + 4 qg + i of key r16 in zt[p][ft][i].
 template <int D, int F, int P>
-__device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)[D / 32], int r16, int qg,
-                                          float (*x)[F / 4])
+__device__ __forceinline__ void z_tiles(const uint16_t* Wl, const bf16x8 (*kb)[D / 32], int r16, int qg,
+                                        floatx4 (*zt)[F / 32])
 {
     constexpr int Fh = F / 2, DS = D / 32, WS = D + 8;  // Wl: [3][Fh][WS] in LDS
-    floatx4 zt[P][Fh / 16];
 #pragma unroll
     for (int ft = 0; ft < Fh / 16; ++ft) {
 #pragma unroll
@@ -88,6 +85,17 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
             }
         }
     }
+}
+
+// phi = [softmax(z); softmax(-z)] from z in the layout z_tiles leaves it (the four
+// lanes of a key combine by lane swaps).  x[p][h] is the feature of operand slot h:
+// slot h = 8 mf + j holds feature 16 (2 mf + j / 4) + 4 qg + j % 4 (positive half for
+// mf < F / 64).  The same arithmetic, in the same order, as the prefill prologue, so
+// that phi recomputed from a stored z equals the prologue's phi bit for bit.
+template <int F, int P>
+__device__ __forceinline__ void phi_from_z(const floatx4 (*zt)[F / 32], float (*x)[F / 4])
+{
+    constexpr int Fh = F / 2;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         float zmax = -INFINITY, zmin = INFINITY;
@@ -113,6 +121,36 @@ __device__ __forceinline__ void phi_tiles(const uint16_t* Wl, const bf16x8 (*kb)
         const float isp = 1.f / sp, isn = 1.f / sn;
 #pragma unroll
         for (int h = 0; h < F / 4; ++h) x[p][h] *= h < Fh / 4 ? isp : isn;
+    }
+}
+
+// stored z of key `row` (natural feature order, Fh floats) in the z_tiles layout
+template <int F>
+__device__ __forceinline__ void load_z(const float* row, int qg, floatx4* zt)
+{
+#pragma unroll
+    for (int ft = 0; ft < F / 32; ++ft) {
+        const float4 z4 = *(const float4*)(row + ft * 16 + qg * 4);
+        zt[ft] = floatx4{z4.x, z4.y, z4.z, z4.w};
+    }
+}
+
+// bf16 hi / lo operand parts of the features in slot order
+template <int F>
+__device__ __forceinline__ void hilo_split(const float* x, bf16x8* bh, bf16x8* bl)
+{
+#pragma unroll
+    for (int mf = 0; mf < F / 32; ++mf) {
+        u16x8 uh, ul;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float xv = x[mf * 8 + j];
+            const uint16_t h = bf16_bits(xv);
+            uh[j] = h;
+            ul[j] = bf16_bits(xv - bf16_val(h));
+        }
+        bh[mf] = __builtin_bit_cast(bf16x8, uh);
+        bl[mf] = __builtin_bit_cast(bf16x8, ul);
     }
 }
 
@@ -153,7 +191,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
     int* misc = (int*)(smem + sm.misc);
     float* mrg = (float*)(smem + sm.stVT);  // merge area, reused after the key loop
     float* nEL = (float*)(smem + sm.nE);    // incremental decode: n of the leaving key, then d at [D]
-    float* phiFop = (float*)(smem + sm.phiFop);
+    float* zE = (float*)(smem + sm.zE);
 
     const int chain = blockIdx.x, b = chain / d.Hkv, g = chain % d.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, qg = lane >> 4;
@@ -224,18 +262,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
     const bool storedScores = INC && incValid && foldStep;
     const int nT = (cnt + 15) / 16;
     const int bw = wave - NA;
-    // features of the cached keys come from the state (hi | lo rows in operand order)
-    uint4 fq[2 * FM];
+    // the cached keys' features are recomputed from their stored z = W k (Fh floats
+    // per key, a quarter of them per lane in the z_tiles layout)
+    floatx4 zq[F / 32];
     uint2 vq[DT];
     auto tile_load = [&](int tt) {
         const int slot = tt * 16 + r16 < cnt ? tt * 16 + r16 : cnt - 1;
-        const uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F + qg * 8;
+        load_z<F>(ch.cz() + (size_t)slot * Fh, qg, zq);
         const bf16* vr = ch.cache_v<bf16>() + (size_t)slot * D;
-#pragma unroll
-        for (int mf = 0; mf < FM; ++mf) {
-            fq[mf] = *(const uint4*)(pr + mf * 32);
-            fq[FM + mf] = *(const uint4*)(pr + F + mf * 32);
-        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vq[dt] = *(const uint2*)(vr + dt * 16 + qg * 4);
     };
@@ -570,28 +604,22 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
             bf16x8 kb[1][DS];
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) kb[0][ks] = __builtin_bit_cast(bf16x8, kEq[ks]);
+            floatx4 zt[1][F / 32];
+            z_tiles<D, F, 1>(Wl, kb, r16, qg, zt);
             float x[1][F / 4];
-            phi_tiles<D, F, 1>(Wl, kb, r16, qg, x);
-            if (r16 == 0)
+            phi_from_z<F, 1>(zt, x);
+            if (r16 == 0) {
 #pragma unroll
                 for (int h = 0; h < F / 4; ++h) phiE[slot_feature(h, qg)] = x[0][h];
+#pragma unroll
+                for (int ft = 0; ft < F / 32; ++ft)
+                    *(float4*)(zE + ft * 16 + qg * 4) = make_float4(zt[0][ft][0], zt[0][ft][1], zt[0][ft][2], zt[0][ft][3]);
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) __hip_atomic_store(&misc[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (hasE && (foldStep || INC)) {
                 bf16x8 bh[1][FM], bl[1][FM];
-#pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    u16x8 uh, ul;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float xv = x[0][mf * 8 + j];
-                        const uint16_t h = bf16_bits(xv);
-                        uh[j] = h;
-                        ul[j] = bf16_bits(xv - bf16_val(h));
-                    }
-                    bh[0][mf] = __builtin_bit_cast(bf16x8, uh);
-                    bl[0][mf] = __builtin_bit_cast(bf16x8, ul);
-                }
+                hilo_split<F>(x[0], bh[0], bl[0]);
                 const float dd = dot_s(bh[0], bl[0]);
                 const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
                 if (INC && lane == 0) nEL[D] = dd;
@@ -613,14 +641,19 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
                 // (slots past the count are scored as stored -- zero or an earlier
                 // pair's finite row -- and their errors are not kept)
                 const bool cv = t0 * 16 + r16 < cnt;
+                // (this tile's z copied out, so the next tile's loads issue before the
+                // features are recomputed)
+                floatx4 zc[1][F / 32];
 #pragma unroll
-                for (int mf = 0; mf < FM; ++mf) {
-                    bh[0][mf] = __builtin_bit_cast(bf16x8, fq[mf]);
-                    bl[0][mf] = __builtin_bit_cast(bf16x8, fq[FM + mf]);
-                }
+                for (int ft = 0; ft < F / 32; ++ft) zc[0][ft] = zq[ft];
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vv[0][dt] = vq[dt];
                 if (t0 + NB < nT) tile_load(t0 + NB);
+                {
+                    float x[1][F / 4];
+                    phi_from_z<F, 1>(zc, x);
+                    hilo_split<F>(x[0], bh[0], bl[0]);
+                }
                 const float dd = dot_s(bh[0], bl[0]);
                 const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
                 float* nout[1] = {nullptr};
@@ -707,20 +740,23 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
             if ((uint32_t)cposL[u] == pos) vi = u;
         for (int o = 32; o > 0; o >>= 1) vi = min(vi, __shfl_xor(vi, o, 64));
         if (lane == 0) misc[0] = vi;
-        // the folded pair: its stored feature row (hi + lo) or the leaving key's
-        // features, and its value
+        // the folded pair: its features (hi + lo) from its stored z, or the leaving
+        // key's features, and its value
         if (vi < cnt) {
-            const uint16_t* pr = ch.cphi() + (size_t)vi * 2 * F;
-            for (int f = lane; f < F; f += 64) {
-                const int q = perm_pos(f);
-                phiF[f] = bf16_val(pr[q]) + bf16_val(pr[F + q]);
-                if (INC) phiFop[q] = phiF[f];
-            }
+            // recomputed from its stored z as the SRE pass computed them (every column
+            // of the tile holds the victim; column 0 writes), hi + lo as in the SRE
+            floatx4 zt[1][F / 32];
+            load_z<F>(ch.cz() + (size_t)vi * Fh, qg, zt[0]);
+            float x[1][F / 4];
+            phi_from_z<F, 1>(zt, x);
+            if (r16 == 0)
+#pragma unroll
+                for (int h = 0; h < F / 4; ++h) {
+                    const uint16_t hb = bf16_bits(x[0][h]);
+                    phiF[slot_feature(h, qg)] = bf16_val(hb) + bf16_val(bf16_bits(x[0][h] - bf16_val(hb)));
+                }
         } else
-            for (int f = lane; f < F; f += 64) {
-                phiF[f] = phiE[f];
-                if (INC) phiFop[perm_pos(f)] = phiE[f];
-            }
+            for (int f = lane; f < F; f += 64) phiF[f] = phiE[f];
         const bf16* vr = vi < cnt ? ch.cache_v<bf16>() + (size_t)vi * D : vE;
         for (int j = lane; j < D; j += 64) xrow[j] = to_f32(vr[j]);
     }
@@ -763,36 +799,39 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
         //      a leaving key that enters the cache brings its own n, d (the last wave
         //      computed them against the step-start state) plus its share of the fold ----
         if (foldStep) {
-            constexpr int PPL = F / 16, DPL = D / 16;
-            const int sub = lane & 15;
-            for (int u = (tid >> 4); u < cnt; u += NT / 16) {
-                if (u == victim) continue;  // (the whole 16-lane group)
-                const uint16_t* pr = ch.cphi() + (size_t)u * 2 * F + sub * PPL;
+            // tiles of 16 cached pairs dealt to the waves: the pair's features from its
+            // stored z as in the SRE pass (hi + lo), kappa = phi . phi_f over the four
+            // lanes of its column, then lane group qg adds kappa v_f to n at rows
+            // qg * D / 4 .. + D / 4
+            constexpr int DQ = D / 4;
+            const int nTc = (cnt + 15) / 16;
+            for (int tt = wave; tt < nTc; tt += NT / 64) {
+                const int u = tt * 16 + r16;
+                const bool cv = u < cnt && u != victim;
+                floatx4 zt[1][F / 32];
+                load_z<F>(ch.cz() + (size_t)(u < cnt ? u : cnt - 1) * Fh, qg, zt[0]);
+                float x[1][F / 4];
+                phi_from_z<F, 1>(zt, x);
                 float kk = 0.f;
 #pragma unroll
-                for (int j = 0; j < PPL; j += 4) {
-                    const uint2 h2 = *(const uint2*)(pr + j), l2 = *(const uint2*)(pr + F + j);
-                    const uint32_t hw[2] = {h2.x, h2.y}, lw[2] = {l2.x, l2.y};
+                for (int h = 0; h < F / 4; ++h) {
+                    const uint16_t hb = bf16_bits(x[0][h]);
+                    kk += (bf16_val(hb) + bf16_val(bf16_bits(x[0][h] - bf16_val(hb)))) * phiF[slot_feature(h, qg)];
+                }
+                kk = quad_sum(kk);
+                if (cv) {
+                    float* nr = ch.cn() + (size_t)u * D + qg * DQ;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float hv = __uint_as_float((i & 1) ? (hw[i >> 1] & 0xffff0000u) : (hw[i >> 1] << 16));
-                        const float lv = __uint_as_float((i & 1) ? (lw[i >> 1] & 0xffff0000u) : (lw[i >> 1] << 16));
-                        kk += (hv + lv) * phiFop[sub * PPL + j + i];
+                    for (int j = 0; j < DQ; j += 4) {
+                        float4 n4 = *(const float4*)(nr + j);
+                        n4.x += kk * xrow[qg * DQ + j];
+                        n4.y += kk * xrow[qg * DQ + j + 1];
+                        n4.z += kk * xrow[qg * DQ + j + 2];
+                        n4.w += kk * xrow[qg * DQ + j + 3];
+                        *(float4*)(nr + j) = n4;
                     }
+                    if (qg == 0) ch.cd()[u] += kk;
                 }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) kk += __shfl_xor(kk, o, 64);
-                float* nr = ch.cn() + (size_t)u * D + sub * DPL;
-#pragma unroll
-                for (int j = 0; j < DPL; j += 4) {
-                    float4 n4 = *(const float4*)(nr + j);
-                    n4.x += kk * xrow[sub * DPL + j];
-                    n4.y += kk * xrow[sub * DPL + j + 1];
-                    n4.z += kk * xrow[sub * DPL + j + 2];
-                    n4.w += kk * xrow[sub * DPL + j + 3];
-                    *(float4*)(nr + j) = n4;
-                }
-                if (sub == 0) ch.cd()[u] += kk;
             }
         }
         const int enter = !hasE ? -1 : (nU <= C ? cnt : (victim < cnt ? victim : -1));
@@ -821,13 +860,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
             ch.cache_k<bf16>()[(size_t)slot * D + j] = kE[j];
             ch.cache_v<bf16>()[(size_t)slot * D + j] = vE[j];
         }
-        uint16_t* pr = ch.cphi() + (size_t)slot * 2 * F;  // its features: hi | lo, operand order
-        for (int f = tid; f < F; f += NT) {
-            const float x = phiE[f];
-            const uint16_t h = bf16_bits(x);
-            pr[perm_pos(f)] = h;
-            pr[F + perm_pos(f)] = bf16_bits(x - bf16_val(h));
-        }
+        for (int f = tid; f < Fh; f += NT) ch.cz()[(size_t)slot * Fh + f] = zE[f];  // its z = W k
     }
     if (w > 0)
         for (int j = tid; j < D; j += NT) {

@@ -19,7 +19,7 @@ constexpr int kMaxCache = 1024;
 constexpr int kMaxChunk = 256;
 constexpr int kMaxCand = kMaxCache + kMaxChunk;  // |cache| + |leaving keys| per interval
 constexpr uint32_t kMagic = 0x414c4f4cu;         // "LOLA"
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 4;
 
 constexpr __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -76,9 +76,9 @@ static_assert(sizeof(StateHeader) == 32, "kernels test the first 32 bytes of a s
 // State buffer: header | W [Hkv][Fh][D] f32 | Wb [Hkv][3][Fh][D] bf16 (three parts of W, largest first) | chains [B][Hkv]
 // chain: tokens seen i64 | cache_count i32 | H^T [D][F] f32 | s [F] f32 | cache_pos [C] i32 |
 //        ring_k [w][D] io | ring_v [w][D] io | cache_k [C][D] io | cache_v [C][D] io |
-//        cache_phi [C][2F] bf16 (bf16 io only: phi of each cached key as hi and lo parts,
-//        each in MFMA operand order, so that a decode step scores the cache without
-//        recomputing the feature map) | cache_score [C] f32 (the score each cached
+//        cache_z [C][Fh] f32 (bf16 io only: z = W k of each cached key, from which a
+//        decode step recomputes phi(k) = [softmax(z); softmax(-z)] without the W
+//        product) | cache_score [C] f32 (the score each cached
 //        pair was kept with; the stale-score policy reads it back) |
 //        incremental decode only: cache_n [C][D] f32 (H^T phi(k) of each cached pair),
 //        cache_d [C] f32 (s . phi(k)); the int32 at chain offset 12 is 1 while they
@@ -88,7 +88,7 @@ static_assert(sizeof(StateHeader) == 32, "kernels test the first 32 bytes of a s
 // position p is p % w.
 struct StateLayout {
     size_t W, Wb, chains, chain_bytes;
-    size_t otok, ocnt, oincv, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocphi, oscore, ocn, ocd;
+    size_t otok, ocnt, oincv, oH, os, ocpos, oring_k, oring_v, ocache_k, ocache_v, ocz, oscore, ocn, ocd;
     size_t total;
 };
 
@@ -112,7 +112,7 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
     s.oring_v = c;   c = align_up(c + (size_t)d.esize * d.w * d.D, 256);
     s.ocache_k = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
     s.ocache_v = c;  c = align_up(c + (size_t)d.esize * d.C * d.D, 256);
-    s.ocphi = c;     c = align_up(c + (d.io == 1 ? sizeof(uint16_t) * 2 * (size_t)d.F * d.C : 0), 256);
+    s.ocz = c;       c = align_up(c + (d.io == 1 ? sizeof(float) * (size_t)d.Fh * d.C : 0), 256);
     s.oscore = c;    c = align_up(c + sizeof(float) * (size_t)(d.C > 0 ? d.C : 1), 256);
     s.ocn = c;       c = align_up(c + (d.inc ? sizeof(float) * (size_t)d.C * d.D : 0), 256);
     s.ocd = c;       c = align_up(c + (d.inc ? sizeof(float) * (size_t)d.C : 0), 256);
@@ -126,7 +126,8 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 //   t0 [B] i64 | phiX [B][Hkv][X][F] f32 | ring0_k/v [B][Hkv][w][D] io |
 //   cache0_k/v [B][Hkv][C][D] io | cphi [B][Hkv][C][F] f32 |
 //   phiS [B][Hkv][X][2F] bf16 | cphiS [B][Hkv][C][2F] bf16 (hi then lo parts of
-//   phi, features in the SRE operand order) |
+//   phi, features in the SRE operand order) | zX [B][Hkv][X][Fh] f32 (bf16 io: z = W k
+//   of each row, for the state's cache_z) |
 //   snapH [B][Hkv][NI][D][F] H^T: f32 for f32 io; bf16 (hi part) in operand order for bf16 io |
 //   snapS [B][Hkv][NI][F] f32 |
 //   snapRef [B][Hkv][NI][C] i32 | snapN [B][Hkv][NI] i32 |
@@ -134,7 +135,7 @@ inline __host__ __device__ StateLayout state_layout(const Dims& d, int B)
 //   xe [B][Hkv][2][D/16][C + L] u64 (per-column-slice partial SRE: exchange
 //      number << 32 | f32 bits; two buffers used alternately)
 struct WsLayout {
-    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, snapH, snapS, snapRef, snapN, xsync, xe;
+    size_t t0, phiX, ring0_k, ring0_v, cache0_k, cache0_v, cphi, phiS, cphiS, zX, snapH, snapS, snapRef, snapN, xsync, xe;
     size_t total;
     int X, NI;
 };
@@ -156,6 +157,7 @@ inline __host__ __device__ WsLayout ws_layout(const Dims& d, int B, int n)
     s.cphi = off;     off = align_up(off + sizeof(float) * ch * Cp * d.F, 256);
     s.phiS = off;     off = align_up(off + sizeof(uint16_t) * ch * s.X * 2 * d.F, 256);
     s.cphiS = off;    off = align_up(off + sizeof(uint16_t) * ch * Cp * 2 * d.F, 256);
+    s.zX = off;       off = align_up(off + (d.io == 1 ? sizeof(float) * ch * s.X * d.Fh : 0), 256);
     s.snapH = off;    off = align_up(off + (size_t)(d.io == 1 ? 2 : 4) * ch * s.NI * d.F * d.D, 256);
     s.snapS = off;    off = align_up(off + sizeof(float) * ch * s.NI * d.F, 256);
     s.snapRef = off;  off = align_up(off + sizeof(int32_t) * ch * s.NI * Cp, 256);

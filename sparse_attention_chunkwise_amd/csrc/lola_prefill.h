@@ -41,7 +41,7 @@ struct Chain {
     template <typename T> __device__ T* ring_v() const { return (T*)(base + sl->oring_v); }
     template <typename T> __device__ T* cache_k() const { return (T*)(base + sl->ocache_k); }
     template <typename T> __device__ T* cache_v() const { return (T*)(base + sl->ocache_v); }
-    __device__ uint16_t* cphi() const { return (uint16_t*)(base + sl->ocphi); }  // bf16 io
+    __device__ float* cz() const { return (float*)(base + sl->ocz); }  // bf16 io: [C][Fh]
     __device__ float* cscore() const { return (float*)(base + sl->oscore); }
     __device__ int32_t& incv() const { return *(int32_t*)(base + sl->oincv); }  // incremental n, d valid
     __device__ float* cn() const { return (float*)(base + sl->ocn); }           // [C][D]
@@ -107,6 +107,11 @@ __device__ __forceinline__ uint16_t* ws_cphiS(const Args& a, int chain, int slot
 {
     int Cp = a.d.C > 0 ? a.d.C : 1;
     return (uint16_t*)(a.ws + a.wl.cphiS) + ((size_t)chain * Cp + slot) * 2 * a.d.F;
+}
+// z = W k of extended row x (bf16 io), natural feature order
+__device__ __forceinline__ float* ws_zX(const Args& a, int chain, int x)
+{
+    return (float*)(a.ws + a.wl.zX) + ((size_t)chain * a.wl.X + x) * a.d.Fh;
 }
 // Operand position of feature f: MFMA step m = f/32, lane group qg = (f%16)/4,
 // slot j = 4*((f/16)%2) + f%4, position m*32 + qg*8 + j.  Lane group qg of an
@@ -349,6 +354,11 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(Args a, int fp32_row
     sp = quad_sum(sp);
     sn = quad_sum(sn);
     if (row >= X + C) return;
+    if (row < X) {  // z of the row (features ft * 16 + 4 qg + i), for the state's cache_z
+        float* zo = ws_zX(a, chain, row);
+#pragma unroll
+        for (int ft = 0; ft < FTH; ++ft) *(float4*)(zo + ft * 16 + qg * 4) = make_float4(zt[ft][0], zt[ft][1], zt[ft][2], zt[ft][3]);
+    }
     const bool valid = src != nullptr;
     const float isp = valid ? 1.f / sp : 0.f, isn = valid ? 1.f / sn : 0.f;
     float ph[2 * FTH][4];  // feature tile T: + half T < FTH, - half T >= FTH
@@ -1065,11 +1075,11 @@ __global__ __launch_bounds__(scan_threads(D)) void scan_kernel(Args a)
         }
     }
     if constexpr (std::is_same<T, bf16>::value) {
-        // feature rows (hi | lo, operand order) of the cache entries added in this call
-        constexpr int PP = 2 * F / 8;
-        for (int q = tid; q < cnt * PP; q += NT) {
-            const int i = q / PP, pc = (q % PP) * 8, code = cref[i];
-            if (code >= 0) *(uint4*)(ch.cphi() + (size_t)i * 2 * F + pc) = *(const uint4*)(ws_phiS(a, chain, code) + pc);
+        // z = W k of the cache entries added in this call
+        constexpr int ZP = F / 2 / 4;
+        for (int q = tid; q < cnt * ZP; q += NT) {
+            const int i = q / ZP, pc = (q % ZP) * 4, code = cref[i];
+            if (code >= 0) *(float4*)(ch.cz() + (size_t)i * (F / 2) + pc) = *(const float4*)(ws_zX(a, chain, code) + pc);
         }
     }
     if (w > 0) {

@@ -915,11 +915,11 @@ __global__ __launch_bounds__(kSplitThreads) void scan_split_kernel(Args a)
                 *(uint4*)(ch.cache_v<bf16>() + (size_t)i * D + pc) = v4;
             }
         }
-        // and their feature rows (hi | lo, operand order), for the decode step's scoring
-        constexpr int PP = 2 * F / 8;
-        for (int q = tid; q < nrc * PP; q += NT) {
-            const int i = rank + nb * (q / PP), pc = (q % PP) * 8, code = cref[i];
-            if (code >= 0) *(uint4*)(ch.cphi() + (size_t)i * 2 * F + pc) = *(const uint4*)(code_phs(code) + pc);
+        // and their z = W k, from which a decode step recomputes the features
+        constexpr int ZP = F / 2 / 4;
+        for (int q = tid; q < nrc * ZP; q += NT) {
+            const int i = rank + nb * (q / ZP), pc = (q % ZP) * 4, code = cref[i];
+            if (code >= 0) *(float4*)(ch.cz() + (size_t)i * (F / 2) + pc) = *(const float4*)(ws_zX(a, chain, code) + pc);
         }
         if (w > 0) {
             const int64_t tend = t0 + ns;
