@@ -56,6 +56,12 @@
  *   - Supported shapes: head_dim 64 or 128; feat_half 32 or 64;
  *     n_q_heads / n_kv_heads <= 16; window <= 8192; cache_cap <= 1024;
  *     chunk <= 256; positions below 2^31 per sequence.
+ *   - Environment: LOLA_SCAN_SPLIT=0 (read at every prefill call) makes bf16
+ *     prefill use the one-workgroup-per-chain scan instead of the split scan;
+ *     LOLA_TRACE=1 (read at the first launch of the process) encloses every
+ *     kernel launch in a roctx range named after the kernel ("lola::prologue",
+ *     "lola::scan_split", "lola::scan", "lola::output", "lola::decode"; the
+ *     roctx library is opened only then, and tracing stays off if it cannot be).
  */
 #ifndef LOLA_H
 #define LOLA_H

@@ -1,5 +1,6 @@
 // C ABI of liblola: argument checks, layouts and kernel launches.
 // Every check happens on the host before anything is enqueued.
+#include <dlfcn.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -53,6 +54,43 @@ lola_status noalloc_scratch(hipStream_t stream, void** out)
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Host-side ranges for profilers: with LOLA_TRACE=1 in the environment every kernel
+// launch is enclosed in a roctx range named after the kernel (rocprofv3 --marker-trace
+// records them).  The roctx library is opened at the first launch and only then;
+// without the variable, or without the library, a launch pays one branch.
+struct Tracer {
+    bool on = false;
+    int (*push)(const char*) = nullptr;
+    int (*pop)() = nullptr;
+};
+const Tracer& tracer()
+{
+    static const Tracer t = [] {
+        Tracer r;
+        const char* e = getenv("LOLA_TRACE");
+        if (!e || strcmp(e, "1") != 0) return r;
+        void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+        if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+        if (!h) return r;
+        r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+        r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+        r.on = r.push && r.pop;
+        return r;
+    }();
+    return t;
+}
+struct TraceRange {
+    bool on;
+    explicit TraceRange(const char* name) : on(tracer().on)
+    {
+        if (on) tracer().push(name);
+    }
+    ~TraceRange()
+    {
+        if (on) tracer().pop();
+    }
+};
 
 lola_status make_dims(const lola_config* cfg, Dims* d)
 {
@@ -177,13 +215,17 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
     }
     const bool split = pu > 0;
     dim3 gp((a.wl.X + d.C + 63) / 64, chains);
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((prologue_bf16_kernel<D, F / 2>), gp, dim3(256), 0, s, a, split ? 0 : 1);
-    else
-        hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
+    {
+        TraceRange tr("lola::prologue");
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((prologue_bf16_kernel<D, F / 2>), gp, dim3(256), 0, s, a, split ? 0 : 1);
+        else
+            hipLaunchKernelGGL((prologue_kernel<D, F / 2, T>), gp, dim3(256), 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess || mark(ev, 1, s) != hipSuccess) return LOLA_ERR_HIP;
     if constexpr (sizeof(T) == 2) {
         if (split) {
+            TraceRange tr("lola::scan_split");
             if (allow_lds(scan_split_kernel<D, F>, split_lds) != hipSuccess) return LOLA_ERR_HIP;
             void* params[] = {&a};
             if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(scan_split_kernel<D, F>),
@@ -193,19 +235,23 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
         }
     }
     if (!split) {
+        TraceRange tr("lola::scan");
         const size_t scan_lds = scan_smem(D, F, d.C, d.L, sizeof(T)).total;
         if (allow_lds(scan_kernel<D, F, T>, scan_lds) != hipSuccess) return LOLA_ERR_HIP;
         hipLaunchKernelGGL((scan_kernel<D, F, T>), dim3(chains), dim3(scan_threads(D)), scan_lds, s, a);
     }
     if (hipGetLastError() != hipSuccess || mark(ev, 2, s) != hipSuccess) return LOLA_ERR_HIP;
-    if constexpr (sizeof(T) == 2) {
-        const int wpi = (d.G * d.L + kOutRows - 1) / kOutRows;
-        const size_t olds = out_smem<D, F>(d.C).total;
-        if (allow_lds(output_kernel_bf16<D, F>, olds) != hipSuccess) return LOLA_ERR_HIP;
-        hipLaunchKernelGGL((output_kernel_bf16<D, F>), dim3(a.NI * wpi, chains), dim3(kOutThreads), olds, s, a);
-    } else {
-        const int wpi = (d.G * d.L + 63) / 64;
-        hipLaunchKernelGGL((output_kernel<D, F, T>), dim3(a.NI * wpi, chains), dim3(256), 0, s, a);
+    {
+        TraceRange tr("lola::output");
+        if constexpr (sizeof(T) == 2) {
+            const int wpi = (d.G * d.L + kOutRows - 1) / kOutRows;
+            const size_t olds = out_smem<D, F>(d.C).total;
+            if (allow_lds(output_kernel_bf16<D, F>, olds) != hipSuccess) return LOLA_ERR_HIP;
+            hipLaunchKernelGGL((output_kernel_bf16<D, F>), dim3(a.NI * wpi, chains), dim3(kOutThreads), olds, s, a);
+        } else {
+            const int wpi = (d.G * d.L + 63) / 64;
+            hipLaunchKernelGGL((output_kernel<D, F, T>), dim3(a.NI * wpi, chains), dim3(256), 0, s, a);
+        }
     }
     if (hipGetLastError() != hipSuccess || mark(ev, 3, s) != hipSuccess) return LOLA_ERR_HIP;
     return LOLA_OK;
@@ -214,6 +260,7 @@ lola_status launch_prefill(Args& a, hipStream_t s, void* const* ev)
 template <int D, int F, typename T>
 lola_status launch_decode(Args& a, hipStream_t s)
 {
+    TraceRange tr("lola::decode");
     if constexpr (sizeof(T) == 2) {
         const size_t lds = dec_smem<D, F>(a.d.C).total;
         if (a.d.inc) {
