@@ -1,11 +1,11 @@
 // Decode step for bf16 io (gfx950): one one-token update interval per
-// (sequence, KV head) chain, one workgroup (4 waves) per chain, state read and
-// written in place.
+// (sequence, KV head) chain, one workgroup of 8 waves per chain (waves 0-3 read,
+// waves 4-7 manage, side by side), state read and written in place.
 //
 //   read   -- the chain's G query heads (MFMA columns) attend with exact
 //             softmax to the window [t-w+1, t] and the cache, streamed in
-//             blocks of 128 keys (32 per wave) with an online softmax per wave,
-//             merged at the end; the linear part is H^T phi(q) / s . phi(q)
+//             groups of 32 keys dealt to the 4 read waves, with an online
+//             softmax per wave, merged at the end; the linear part is H^T phi(q) / s . phi(q)
 //             plus the key at t-w that leaves the window at this step (the new
 //             key itself when w = 0); one shared denominator (LoLA summary,
 //             "Inferentiestrategie", step 4).
@@ -27,7 +27,7 @@
 
 namespace lola {
 
-constexpr int kDecBlock = 128;  // keys staged per block (32 per wave)
+constexpr int kDecBlock = 128;  // V^T staging columns: 32 keys per read wave
 
 struct DecSmem {
     size_t HhT, HlT, Wl, sP, sParts, cposL, esc, phiE, phiF, xrow, stVT, nE, zE, misc, total;
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
             }
         }
         // the cache in tiles of 16 slots dealt to the management waves in turn; each
-        // tile's feature and value rows load while the previous tile is scored
+        // tile's z and value rows load while the previous tile is scored
         if (scoreCache) {
             for (int t0 = bw; t0 < nT; t0 += NB) {
                 bf16x8 bh[1][FM], bl[1][FM];

@@ -2,7 +2,8 @@
 //
 // One lola_prefill_chunk call runs three launches on the caller's stream:
 //   1. prologue  -- feature rows phi(k) for the window keys at the call start
-//                   and the new keys; copies of the window ring and the cache
+//                   and the new keys (and, bf16 io, their z = W k for the
+//                   state's cache); copies of the window ring and the cache
 //                   as they stand at the call start (the scan rewrites them).
 //   2. scan      -- one workgroup per (sequence, KV head) chain walks the
 //                   update intervals in order: snapshot (H, s, cache) at the
