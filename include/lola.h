@@ -56,6 +56,10 @@
  *   - Supported shapes: head_dim 64 or 128; feat_half 32 or 64;
  *     n_q_heads / n_kv_heads <= 16; window <= 8192; cache_cap <= 1024;
  *     chunk <= 256; positions below 2^31 per sequence.
+ *   - bf16 prefill with the default policy runs the split scan as a
+ *     cooperative launch; where that launch is refused (observed: a second
+ *     process on a GPU whose first process has run split scans) the call
+ *     returns LOLA_ERR_HIP, and LOLA_SCAN_SPLIT=0 avoids it.
  *   - Environment: LOLA_SCAN_SPLIT=0 (read at every prefill call) makes bf16
  *     prefill use the one-workgroup-per-chain scan instead of the split scan;
  *     LOLA_TRACE=1 (read at the first launch of the process) encloses every

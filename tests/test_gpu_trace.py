@@ -1,7 +1,11 @@
 """LOLA_TRACE=1 (a roctx range around every kernel launch) must not change any result:
 the same small prefill and decode steps run in two child processes, one with the
 variable set, and their outputs and final state bytes must be equal (needs an MI355X).
-Without a profiler attached the roctx calls record nothing."""
+Without a profiler attached the roctx calls record nothing.
+
+The children use the one-workgroup scan (LOLA_SCAN_SPLIT=0): the split scan's
+cooperative launch failed (LOLA_ERR_HIP) in a child while this test process, which had
+run split scans in earlier tests, was alive on the same GPU."""
 import hashlib
 import os
 import subprocess
@@ -40,6 +44,7 @@ print("digest", h.hexdigest(), flush=True)
 def _digest(trace: bool) -> str:
     env = dict(os.environ)
     env.pop("LOLA_TRACE", None)
+    env["LOLA_SCAN_SPLIT"] = "0"
     if trace:
         env["LOLA_TRACE"] = "1"
     res = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT)], env=env, capture_output=True, text=True,
