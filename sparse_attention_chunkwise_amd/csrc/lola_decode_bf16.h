@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
             sParts[2 * F + o] = bf16_bits(r1 - bf16_val(p2));
         }
         for (int i = tid; i < cnt; i += NT) cposL[i] = ch.cpos()[i];
-        if (tid == 0) misc[1] = 0;  // set once the leaving key's features are in LDS
+        if (tid == 0) {
+            misc[1] = 0;   // set once the leaving key's features are in LDS
+            misc[2] = NB;  // next cache tile to score (tiles 0 .. NB - 1 go to the management waves)
+        }
     }
     // query frags (read waves, columns r16 < G); the leaving key's row (last wave,
     // column 0) and its value rows dt * 16 + 4 qg .. + 3 (wave 0 and the last wave)
@@ -632,41 +635,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
                 if (lane == 0) esc[cnt] = e[0];
             }
         }
-        // the cache in tiles of 16 slots dealt to the management waves in turn; each
-        // tile's z and value rows load while the previous tile is scored
-        if (scoreCache) {
-            for (int t0 = bw; t0 < nT; t0 += NB) {
-                bf16x8 bh[1][FM], bl[1][FM];
-                uint2 vv[1][DT];
-                // (slots past the count are scored as stored -- zero or an earlier
-                // pair's finite row -- and their errors are not kept)
-                const bool cv = t0 * 16 + r16 < cnt;
-                // (this tile's z copied out, so the next tile's loads issue before the
-                // features are recomputed)
-                floatx4 zc[1][F / 32];
-#pragma unroll
-                for (int ft = 0; ft < F / 32; ++ft) zc[0][ft] = zq[ft];
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vv[0][dt] = vq[dt];
-                if (t0 + NB < nT) tile_load(t0 + NB);
-                {
-                    float x[1][F / 4];
-                    phi_from_z<F, 1>(zc, x);
-                    hilo_split<F>(x[0], bh[0], bl[0]);
-                }
-                const float dd = dot_s(bh[0], bl[0]);
-                const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
-                float* nout[1] = {nullptr};
-                if (INC && cv) {  // the stored n, d of this cached pair, computed afresh
-                    const int slot = t0 * 16 + r16;
-                    nout[0] = ch.cn() + (size_t)slot * D;
-                    if (qg == 0) ch.cd()[slot] = dd;
-                }
-                float e[1];
-                sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, vv, e, nout);
-                if (qg == 0 && cv) esc[t0 * 16 + r16] = e[0];
-            }
-        }
         if constexpr (INC) {
             if (storedScores) {
                 // e = |n / d - v|^2 from the stored n, d: 16 lanes per cached pair, D / 16
@@ -695,6 +663,50 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel_bf16(Args a)
                     if (sub == 0) esc[u] = e;
                 }
             }
+        }
+    }
+    // ---- the cache in tiles of 16 slots: each management wave starts with its own
+    //      tile, then every wave takes the next unscored tile from an LDS counter as it
+    //      frees up (the read waves once their key groups are done); a tile's z and
+    //      value rows load while the previous tile is scored ----
+    if (scoreCache) {
+        auto grab = [&]() -> int {
+            int v = 0;
+            if (lane == 0) v = __hip_atomic_fetch_add(&misc[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return __builtin_amdgcn_readfirstlane(v);
+        };
+        int tcur = rd ? grab() : bw;
+        if (rd && tcur < nT) tile_load(tcur);
+        while (tcur < nT) {
+            bf16x8 bh[1][FM], bl[1][FM];
+            uint2 vv[1][DT];
+            // (slots past the count are scored as stored -- zero or an earlier
+            // pair's finite row -- and their errors are not kept)
+            const bool cv = tcur * 16 + r16 < cnt;
+            floatx4 zc[1][F / 32];
+#pragma unroll
+            for (int ft = 0; ft < F / 32; ++ft) zc[0][ft] = zq[ft];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vv[0][dt] = vq[dt];
+            const int tnext = grab();
+            if (tnext < nT) tile_load(tnext);
+            {
+                float x[1][F / 4];
+                phi_from_z<F, 1>(zc, x);
+                hilo_split<F>(x[0], bh[0], bl[0]);
+            }
+            const float dd = dot_s(bh[0], bl[0]);
+            const float inv[1] = {dd > 0.f ? 1.f / dd : 0.f};
+            float* nout[1] = {nullptr};
+            if (INC && cv) {  // the stored n, d of this cached pair, computed afresh
+                const int slot = tcur * 16 + r16;
+                nout[0] = ch.cn() + (size_t)slot * D;
+                if (qg == 0) ch.cd()[slot] = dd;
+            }
+            float e[1];
+            sre_core(std::integral_constant<int, 1>{}, bh, bl, inv, vv, e, nout);
+            if (qg == 0 && cv) esc[tcur * 16 + r16] = e[0];
+            tcur = tnext;
         }
     }
     // the read's parts are final and the staging area is free; all SRE in LDS (the
